@@ -1,0 +1,134 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module only draws random tensors and masks; it holds none of the
+attention arithmetic, so both the HIP path's tests/bench and the CPU oracle
+can take their inputs from it.  All draws are fp32 ``torch.randn`` /
+``torch.rand`` on the CPU from a seeded ``torch.Generator``, then rounded to
+the workload's dtype (round-to-nearest-even); every consumer reads the same
+rounded values.
+
+Workloads (B, H, N, d; dtype; masking):
+
+=============================  ==========================  =====  ==================
+name                           shape                       dtype  structure
+=============================  ==========================  =====  ==================
+dense_n256_d64_f32             1, 1, 256, 64               f32    dense, fwd only
+dense_n4096_d64_f32            1, 1, 4096, 64              f32    dense, fwd only
+dense_n4096_d64_bf16           1, 1, 4096, 64              bf16   same draws as f32
+causal_b4h12_n8192_d64_bf16    4, 12, 8192, 64             bf16   causal, fwd+bwd
+causal_b1h12_n23400_d64_f16    1, 12, 23400, 64            f16    causal, drift
+sparse_b2h16_n16384_d128_bf16  2, 16, 16384, 128           bf16   128x128 block mask
+=============================  ==========================  =====  ==================
+
+* Values are N(0, 1).  The N=4096 pair repeats the ultralytics glossary
+  page's own loop inputs: seed 0, one ``randn(3, n, d)`` unbound into q, k, v.
+* The long-context fp16 workload (one trading day at 1 s resolution: 23 400
+  steps, the length the marketmaker.cc page motivates) adds a slow drift
+  0.01 * t / N to row t of Q, K and V before rounding; dO has no drift.
+* The block-sparse mask is Bernoulli(0.25) over 128 x 128 tiles with the
+  diagonal tiles always kept, one mask for every (b, h).
+* Scale is 1/sqrt(d) rounded to fp32 (0.125 exactly for d = 64).
+"""
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import torch
+
+TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+MASK_BLOCK = 128
+
+
+def scale_for(d: int) -> float:
+    """1/sqrt(d) rounded to fp32, as a Python float (exactly representable)."""
+    return float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32).item())
+
+
+@dataclass
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str
+    causal: bool
+    backward: bool
+    seed: int
+    drift: float = 0.0
+    mask_frac: Optional[float] = None
+    mask_seed: Optional[int] = None
+    page_layout: bool = False          # randn(3, n, d) draw order of the glossary page
+    notes: str = field(default="")
+
+    @property
+    def scale(self) -> float:
+        return scale_for(self.d)
+
+    @property
+    def sparse(self) -> bool:
+        return self.mask_frac is not None
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("dense_n256_d64_f32", 1, 1, 256, 64, "f32", False, False, seed=1),
+        Workload("dense_n4096_d64_f32", 1, 1, 4096, 64, "f32", False, False, seed=0,
+                 page_layout=True),
+        Workload("dense_n4096_d64_bf16", 1, 1, 4096, 64, "bf16", False, False, seed=0,
+                 page_layout=True),
+        Workload("causal_b4h12_n8192_d64_bf16", 4, 12, 8192, 64, "bf16", True, True, seed=3),
+        Workload("causal_b1h12_n23400_d64_f16", 1, 12, 23400, 64, "f16", True, True, seed=4,
+                 drift=0.01),
+        Workload("sparse_b2h16_n16384_d128_bf16", 2, 16, 16384, 128, "bf16", False, True,
+                 seed=5, mask_frac=0.25, mask_seed=50),
+    ]
+}
+
+HEADLINE = "causal_b4h12_n8192_d64_bf16"
+
+
+def draw_qkvdo(B, H, N, d, dtype="bf16", seed=0, drift=0.0, with_do=True):
+    """Seeded (q, k, v, dO) of shape (B, H, N, d) in `dtype` (CPU tensors).
+
+    One fp32 ``randn(4 or 3, B, H, N, d)`` draw; with drift, row t of q, k, v
+    gets + drift * t / N before rounding.
+    """
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((4 if with_do else 3, B, H, N, d), generator=g, dtype=torch.float32)
+    if drift:
+        t = torch.arange(N, dtype=torch.float32).view(N, 1) * (drift / N)
+        x[:3] += t
+    x = x.to(TORCH_DTYPES[dtype])
+    return tuple(x.unbind(0)) + ((None,) if not with_do else ())
+
+
+def draw_page_qkv(n, d, seed=0):
+    """q, k, v as the glossary page draws them: seed, randn(3, n, d).unbind(0)."""
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn((3, n, d), generator=g, dtype=torch.float32).unbind(0)
+
+
+def draw_block_mask(N, frac, seed, keep_diagonal=True, block=MASK_BLOCK):
+    """uint8 [ceil(N/block)][ceil(N/block)]: Bernoulli(frac) tiles, diagonal kept."""
+    t = -(-N // block)
+    g = torch.Generator().manual_seed(seed)
+    m = torch.rand((t, t), generator=g) < frac
+    if keep_diagonal:
+        m |= torch.eye(t, dtype=torch.bool)
+    return m.to(torch.uint8)
+
+
+def make(name: str):
+    """Inputs of a named workload: dict with q, k, v, do (or None), mask, ..."""
+    w = WORKLOADS[name]
+    if w.page_layout:
+        q, k, v = draw_page_qkv(w.N, w.d, w.seed)
+        q, k, v = (t.view(1, 1, w.N, w.d).to(TORCH_DTYPES[w.dtype]) for t in (q, k, v))
+        do = None
+    else:
+        q, k, v, do = draw_qkvdo(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.drift,
+                                 with_do=w.backward)
+    mask = draw_block_mask(w.N, w.mask_frac, w.mask_seed) if w.sparse else None
+    return dict(workload=w, q=q, k=k, v=v, do=do, mask=mask, scale=w.scale, causal=w.causal)

@@ -1,0 +1,42 @@
+"""Plain fp64 CPU oracle for exact attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or
+links this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may use it.  It shares no code with the
+HIP kernels or their host library.
+
+Pages cited in this package (the reader has these pages):
+
+* "Attention flash et question de longueur de séquence" (marketmaker.cc blog,
+  French) -- sections "L'algorithme Flash Attention", "La récurrence softmax
+  en ligne", "Passe arrière", "FA2 : parallélisme", "Le masquage causal".
+* "Flash Attention" (ultralytics.com glossary, French) -- section
+  "Fonctionnement de Flash Attention" and its PyTorch loop.
+* "Почему Flash Attention быстрее" (sloger.press, Russian) -- sections
+  "Проблема — трафик", "Online softmax".
+* "FlashAttention: Fast and Memory-Efficient Exact Attention with
+  IO-Awareness", reading guide (xyznot.com, Portuguese) -- sections
+  "Problema e motivação", "Método" (incremental softmax equations and the
+  four per-block steps), "Extensão: Block-Sparse FlashAttention".
+
+Every function in this package has at least one pin in
+``tests/test_oracle_*.py`` that checks it against something other than
+itself (closed forms, invariants, finite differences, an independent
+library route, brute force, or the worked example one page prints).
+No function is "parity unpinned".
+"""
+
+from .attention import (  # noqa: F401
+    MASK_BLOCK,
+    allowed,
+    forward,
+    forward_head,
+    backward,
+    backward_head,
+    rowsum_do_o,
+)
+from .online import (  # noqa: F401
+    merge_stats,
+    online_softmax_normalised_each_step,
+    online_softmax_deferred,
+)

@@ -1,0 +1,150 @@
+"""Pins for the oracle's backward pass (oracle/attention.py).
+
+The pages only say that the backward pass recomputes S and P from Q, K and
+the saved statistics; the gradient formulas are the softmax chain rule.  They
+are pinned here by central finite differences of L = sum(dO * O) in float64,
+by torch autograd through torch's own attention routine, by closed-form
+special cases and by invariants that hold at any size.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.attention import backward_head, forward_head
+
+RNG = np.random.default_rng(4321)
+
+
+def randn(*shape):
+    return RNG.standard_normal(shape)
+
+
+def loss(q, k, v, do, scale, causal, bm, mb):
+    o, _ = forward_head(q, k, v, scale, causal=causal, block_mask=bm, mask_block=mb)
+    return float(np.sum(do * o))
+
+
+def finite_difference_grads(q, k, v, do, scale, causal, bm, mb, h=1e-5):
+    grads = []
+    for which in range(3):
+        args = [q.copy(), k.copy(), v.copy()]
+        g = np.zeros_like(args[which])
+        for idx in np.ndindex(g.shape):
+            x0 = args[which][idx]
+            args[which][idx] = x0 + h
+            lp = loss(*args, do, scale, causal, bm, mb)
+            args[which][idx] = x0 - h
+            lm = loss(*args, do, scale, causal, bm, mb)
+            args[which][idx] = x0
+            g[idx] = (lp - lm) / (2 * h)
+        grads.append(g)
+    return grads
+
+
+CASES = [
+    # n, d, causal, masked
+    (16, 8, False, False),
+    (16, 8, True, False),
+    (16, 8, False, True),
+    (13, 8, True, True),
+    (16, 64, True, False),
+]
+
+
+@pytest.mark.parametrize("n,d,causal,masked", CASES)
+def test_gradients_match_finite_differences(n, d, causal, masked):
+    q, k, v, do = randn(n, d), randn(n, d), randn(n, d), randn(n, d)
+    mb, bm = 4, None
+    if masked:
+        t = -(-n // mb)
+        bm = (np.random.default_rng(n).random((t, t)) < 0.5).astype(np.uint8)
+        np.fill_diagonal(bm, 1)
+    scale = 1.0 / np.sqrt(d)
+    dq, dk, dv = backward_head(q, k, v, do, scale, causal, bm, mb, chunk=5)
+    fq, fk, fv = finite_difference_grads(q, k, v, do, scale, causal, bm, mb)
+    for got, ref in ((dq, fq), (dk, fk), (dv, fv)):
+        err = np.max(np.abs(got - ref)) / max(1e-12, np.max(np.abs(ref)))
+        assert err <= 1e-6, err
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("masked", [False, True])
+def test_gradients_match_torch_autograd_fp64(causal, masked):
+    n, d, mb = 160, 16, 32
+    q, k, v, do = randn(n, d), randn(n, d), randn(n, d), randn(n, d)
+    bm = None
+    if masked:
+        bm = (np.random.default_rng(8).random((5, 5)) < 0.4).astype(np.uint8)
+        np.fill_diagonal(bm, 1)
+    dq, dk, dv = backward_head(q, k, v, do, 0.3, causal, bm, mb, chunk=37)
+    ok = torch.from_numpy(oracle.allowed(np.arange(n), n, causal, bm, mb))
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_() for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq[None], tk[None], tv[None], attn_mask=ok[None], scale=0.3)[0]
+    o.backward(torch.from_numpy(do))
+    for got, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        np.testing.assert_allclose(got, ref.numpy(), rtol=0, atol=1e-12)
+
+
+def test_gradient_invariants():
+    """sum_j dK_j = 0, sum_j dV_j = sum_i dO_i, D_i = sum_j P_ij dP_ij."""
+    n, d = 300, 32
+    q, k, v, do = randn(n, d), randn(n, d), randn(n, d), randn(n, d)
+    for causal in (False, True):
+        dq, dk, dv = backward_head(q, k, v, do, 0.2, causal, chunk=64)
+        np.testing.assert_allclose(dk.sum(axis=0), 0.0, rtol=0, atol=1e-11)
+        np.testing.assert_allclose(dv.sum(axis=0), do.sum(axis=0), rtol=0, atol=1e-11)
+        o, lse = forward_head(q, k, v, 0.2, causal=causal)
+        s = 0.2 * (q @ k.T)
+        ok = oracle.allowed(np.arange(n), n, causal)
+        p = np.where(ok, np.exp(s - lse[:, None]), 0.0)
+        dp = do @ v.T
+        np.testing.assert_allclose(oracle.rowsum_do_o(do, o), (p * dp).sum(axis=1),
+                                   rtol=0, atol=1e-12)
+
+
+def test_single_token_gradients():
+    q, k, v, do = randn(1, 64), randn(1, 64), randn(1, 64), randn(1, 64)
+    dq, dk, dv = backward_head(q, k, v, do, 0.125)
+    assert np.max(np.abs(dq)) <= 1e-13 and np.max(np.abs(dk)) <= 1e-13
+    np.testing.assert_allclose(dv, do, rtol=0, atol=1e-15)
+
+
+def test_identical_keys_and_constant_values():
+    n, d = 100, 16
+    q, v, do = randn(n, d), randn(n, d), randn(n, d)
+    k = np.tile(randn(1, d), (n, 1))
+    for causal in (False, True):
+        dq, _, _ = backward_head(q, k, v, do, 0.25, causal)
+        assert np.max(np.abs(dq)) <= 1e-13       # scores don't depend on which key
+    k = randn(n, d)
+    vc = np.tile(randn(1, d), (n, 1))
+    for causal in (False, True):
+        dq, dk, _ = backward_head(q, k, vc, do, 0.25, causal)
+        assert np.max(np.abs(dq)) <= 1e-13 and np.max(np.abs(dk)) <= 1e-13
+
+
+def test_fully_masked_rows_contribute_nothing():
+    n, d, mb = 8, 4, 4
+    mask = np.array([[0, 0], [1, 1]], np.uint8)
+    q, k, v, do = randn(n, d), randn(n, d), randn(n, d), randn(n, d)
+    dq, dk, dv = backward_head(q, k, v, do, 0.5, False, mask, mb)
+    assert np.all(dq[:4] == 0)
+    do2 = do.copy()
+    do2[:4] = 1e3 * randn(4, d)                  # upstream grads of empty rows are ignored
+    _, dk2, dv2 = backward_head(q, k, v, do2, 0.5, False, mask, mb)
+    np.testing.assert_allclose(dk, dk2, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dv, dv2, rtol=0, atol=1e-13)
+
+
+def test_batched_wrapper_matches_heads():
+    shp = (2, 2, 30, 8)
+    q, k, v, do = randn(*shp), randn(*shp), randn(*shp), randn(*shp)
+    g = oracle.backward(q, k, v, do, 0.3, causal=True)
+    for b in range(2):
+        for h in range(2):
+            gh = backward_head(q[b, h], k[b, h], v[b, h], do[b, h], 0.3, True)
+            for x, y in zip(g, gh):
+                np.testing.assert_array_equal(x[b, h], y)
