@@ -1,0 +1,118 @@
+// Host side of libfa.so: argument validation and kernel dispatch for the C ABI
+// declared in include/fa.h.  Every check runs before anything is enqueued; an
+// unsupported request returns an error and never runs another code path.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/fa.h"
+#include "fa_kernels.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_common(int B, int H, int N, int d, float scale, int dtype) {
+  if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // Grid sizes and per-head element counts must fit the kernels' int indexing.
+  const long long bh = (long long)B * H;
+  if (bh > (1LL << 24) || (long long)N * d > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
+  if (bh * ((N + 31) / 32) > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+int tensor_ptr_ok(const void* p) { return p != nullptr && aligned(p, 16); }
+
+size_t delta_bytes(int B, int H, int N) {
+  const size_t b = (size_t)B * H * N * sizeof(float);
+  return (b + 255) / 256 * 256;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return 1; }
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad size, dtype or scale)";
+    case FA_ERR_UNSUPPORTED: return "unsupported request (head dim must be 64 or 128; size limits; dtype)";
+    case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_backward_workspace_size()";
+    case FA_ERR_HIP: return "HIP runtime error at kernel launch";
+    default: return "unknown status";
+  }
+}
+
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal,
+               const uint8_t* block_mask, int dtype, void* stream) {
+  if (!tensor_ptr_ok(q) || !tensor_ptr_ok(k) || !tensor_ptr_ok(v) || !tensor_ptr_ok(o))
+    return FA_ERR_INVALID_ARG;
+  if (lse == nullptr || !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
+  const int rc = check_common(B, H, N, d, scale, dtype);
+  if (rc != FA_OK) return rc;
+  fa::FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.mask = block_mask;
+  p.BH = B * H;
+  p.N = N;
+  p.mask_tiles = (N + fa::MASK_TILE - 1) / fa::MASK_TILE;
+  p.scale = scale;
+  p.scale_log2e = scale * kLog2e;
+  const hipError_t e = fa::launch_forward(p, dtype, d, causal != 0, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_backward_workspace_size(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
+  return delta_bytes(B, H, N);
+}
+
+int fa_backward(const void* q, const void* k, const void* v, const void* o,
+                const void* dO, const float* lse,
+                float* dq, float* dk, float* dv,
+                int B, int H, int N, int d, float scale, int causal,
+                const uint8_t* block_mask, int dtype,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!tensor_ptr_ok(q) || !tensor_ptr_ok(k) || !tensor_ptr_ok(v) || !tensor_ptr_ok(o) ||
+      !tensor_ptr_ok(dO) || !tensor_ptr_ok(dq) || !tensor_ptr_ok(dk) || !tensor_ptr_ok(dv))
+    return FA_ERR_INVALID_ARG;
+  if (lse == nullptr || !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
+  const int rc = check_common(B, H, N, d, scale, dtype);
+  if (rc != FA_OK) return rc;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (workspace == nullptr || !aligned(workspace, 16) ||
+      workspace_bytes < fa_backward_workspace_size(B, H, N, d))
+    return FA_ERR_WORKSPACE;
+  fa::BwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dO = dO;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.delta = (float*)workspace;
+  p.mask = block_mask;
+  p.BH = B * H;
+  p.N = N;
+  p.mask_tiles = (N + fa::MASK_TILE - 1) / fa::MASK_TILE;
+  p.scale = scale;
+  p.scale_log2e = scale * kLog2e;
+  const hipError_t e = fa::launch_backward(p, dtype, d, causal != 0, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,96 @@
+// Device-side helpers shared by the gfx950 attention kernels.
+//
+// Matrix-core conventions (checked on the device before these kernels were
+// written).  For v_mfma_f32_32x32x16_{bf16,f16}, C[32x32] += A[32x16] B[16x32]:
+//   A operand, lane l: row i = l % 32, elements e = 0..7 -> k = 8 * (l / 32) + e
+//   B operand, lane l: col j = l % 32, elements e = 0..7 -> k = 8 * (l / 32) + e
+//   C/D, lane l, register r = 0..15: col j = l % 32,
+//        row i = 8 * (r / 4) + 4 * (l / 32) + r % 4
+// For v_mfma_f32_16x16x32_{bf16,f16}, C[16x16] += A[16x32] B[32x16]: A lane l
+// holds row l % 16, k = 8 * (l / 16) + e; B lane l holds column l % 16, same k;
+// C lane l, register r = 0..3: column l % 16, row 4 * (l / 16) + r.
+// For v_mfma_f32_32x32x2_f32: A lane l holds A[l % 32][l / 32], B lane l holds
+// B[l / 32][l % 32], same C layout.
+// The contraction index only has to be paired the same way in A and B, so
+// kernels are free to assign any k order to (l / 32, e) as long as both
+// operands agree.
+//
+// ds_read_b64_tr_b16 (LDS transpose read), per group of 16 lanes: if lane s
+// of the group points at 4 consecutive 16-bit elements, lane t of the group
+// receives element (t % 4) of the rows pointed to by lanes t/4, t/4+4, t/4+8,
+// t/4+12.  With lane s pointing at X[kb + s/4][nb + 4*(s%4)] of a row-major
+// matrix X, lane t receives X[kb + 0..3][nb + t]: a column of four
+// consecutive rows, which is the operand layout an MFMA needs when the
+// contraction runs along X's rows.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+template <typename T> struct V8;
+template <> struct V8<__bf16> { typedef bf16x8 t; typedef bf16x4 h; };
+template <> struct V8<_Float16> { typedef f16x8 t; typedef f16x4 h; };
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32x32x16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32x32x2(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Transpose read of four 16-bit values (see the header comment).
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+template <typename VT>
+__device__ __forceinline__ VT cat_tr16(i16x4 lo, i16x4 hi) {
+  i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(VT, v);
+}
+
+// Reductions across the two 32-lane halves of a wave: every lane gets the
+// combination of its own value and the value of lane (l ^ 32).
+__device__ __forceinline__ float half_swap_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroup index -> logical tile index.  The hardware hands consecutive
+// workgroup ids to the 8 XCDs round robin; this mapping gives each XCD a
+// contiguous range of logical ids so tiles of one head share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+  constexpr int NX = 8;
+  const int x = bid % NX, r = bid / NX;
+  const int per = total / NX, rem = total % NX;
+  return (x < rem) ? x * (per + 1) + r : rem * (per + 1) + (x - rem) * per + r;
+}
+
+}  // namespace fa

@@ -1,0 +1,141 @@
+"""Thin Python binding of libfa.so, the gfx950 attention library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of ``include/fa.h``.  torch provides device memory and
+the current stream.  Importing this module raises ImportError when the
+library has not been built (there is no other code path).
+
+    from exact_io_aware_34_amd import fa
+    o, lse = fa.forward(q, k, v, causal=True)
+    dq, dk, dv = fa.backward(q, k, v, o, lse, do, causal=True)
+"""
+
+import ctypes
+import os
+
+import torch  # loads torch's HIP runtime first, so libfa.so binds to the same one
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libfa.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing; build it with `python -m exact_io_aware_34_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_vp, _i, _f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+_lib.fa_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _i, _vp]
+_lib.fa_forward.restype = _i
+_lib.fa_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                             _i, _i, _i, _i, _f, _i, _vp, _i, _vp, ctypes.c_size_t, _vp]
+_lib.fa_backward.restype = _i
+_lib.fa_backward_workspace_size.argtypes = [_i, _i, _i, _i]
+_lib.fa_backward_workspace_size.restype = ctypes.c_size_t
+_lib.fa_status_string.argtypes = [_i]
+_lib.fa_status_string.restype = ctypes.c_char_p
+_lib.fa_abi_version.restype = _i
+
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+DTYPE_CODES = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+MASK_BLOCK = 128
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"libfa status {status}: {status_string(status)}")
+
+
+def status_string(status: int) -> str:
+    return _lib.fa_status_string(status).decode()
+
+
+def abi_version() -> int:
+    return _lib.fa_abi_version()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check_inputs(*ts):
+    ref = ts[0]
+    if ref.dim() != 4:
+        raise ValueError("tensors must be (batch, heads, seq, head_dim)")
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on a GPU")
+        if t.shape != ref.shape or t.dtype != ref.dtype:
+            raise ValueError("q, k, v (and o, dO) must share shape and dtype")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    if ref.dtype not in DTYPE_CODES:
+        raise ValueError(f"unsupported dtype {ref.dtype}")
+
+
+def _mask_arg(block_mask, n):
+    if block_mask is None:
+        return None
+    t = -(-n // MASK_BLOCK)
+    if block_mask.dtype != torch.uint8 or tuple(block_mask.shape) != (t, t):
+        raise ValueError(f"block_mask must be uint8 of shape ({t}, {t})")
+    if not block_mask.is_cuda or not block_mask.is_contiguous():
+        raise ValueError("block_mask must be a contiguous GPU tensor")
+    return block_mask
+
+
+def default_scale(d: int) -> float:
+    return float(torch.tensor(d ** -0.5, dtype=torch.float32))
+
+
+def forward(q, k, v, causal=False, scale=None, block_mask=None, out=None, lse=None,
+            stream=None):
+    """Exact attention forward: returns (o, lse) with o in q's dtype, lse fp32."""
+    _check_inputs(q, k, v)
+    B, H, N, d = q.shape
+    scale = default_scale(d) if scale is None else float(scale)
+    mask = _mask_arg(block_mask, N)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_inputs(q, o)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 (B, H, N)")
+    rc = _lib.fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                         scale, int(bool(causal)), _ptr(mask), DTYPE_CODES[q.dtype],
+                         _stream(stream))
+    if rc != 0:
+        raise FAError(rc)
+    return o, lse
+
+
+def workspace_size(B, H, N, d) -> int:
+    return int(_lib.fa_backward_workspace_size(B, H, N, d))
+
+
+def backward(q, k, v, o, lse, do, causal=False, scale=None, block_mask=None,
+             workspace=None, grads=None, stream=None):
+    """Exact attention backward: returns fp32 (dq, dk, dv)."""
+    _check_inputs(q, k, v, o, do)
+    B, H, N, d = q.shape
+    scale = default_scale(d) if scale is None else float(scale)
+    mask = _mask_arg(block_mask, N)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 (B, H, N)")
+    if grads is None:
+        grads = tuple(torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+                      for _ in range(3))
+    ws_bytes = workspace_size(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    dq, dk, dv = grads
+    rc = _lib.fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                          _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, scale,
+                          int(bool(causal)), _ptr(mask), DTYPE_CODES[q.dtype],
+                          _ptr(workspace), workspace.numel() * workspace.element_size(),
+                          _stream(stream))
+    if rc != 0:
+        raise FAError(rc)
+    return dq, dk, dv

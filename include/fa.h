@@ -1,0 +1,107 @@
+/*
+ * fa.h -- C ABI of libfa.so: exact attention softmax(scale * Q K^T) V on one
+ * AMD Instinct MI355X (gfx950), forward and backward, with causal and
+ * block-sparse masking.
+ *
+ * The operation is the one the FlashAttention pages define:
+ *   - "FlashAttention: Fast and Memory-Efficient Exact Attention with
+ *     IO-Awareness" reading guide (xyznot.com), section "Método": Q, K, V are
+ *     N x d per head; the forward pass keeps a running row max m and row sum l
+ *     per query (incremental softmax equations), writes O and the softmax
+ *     statistics only; section "Ideias centrais", "Recomputação no Backward
+ *     Pass": the backward pass recomputes S and P from Q, K and the saved
+ *     statistics; section "Extensão: Block-Sparse FlashAttention": a {0,1}
+ *     mask over (query tile, key tile) pairs selects the tiles evaluated.
+ *   - "Attention flash et question de longueur de séquence" (marketmaker.cc),
+ *     section "L'intégration est de huit lignes": tensors are laid out
+ *     (batch, heads, seq, head_dim); section "Le masquage causal": the causal
+ *     mask is built by the kernel, key j is visible to query i iff j <= i.
+ *
+ * Conventions shared by every call
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates nothing and keeps no mutable global state, so calls on
+ *     different streams may run concurrently.
+ *   - Tensors are contiguous, row-major (B, H, N, d) with d fastest; lse and
+ *     the backward workspace's per-row terms are (B, H, N).  Pointers must be
+ *     16-byte aligned.
+ *   - `dtype` (fa_dtype) is the element type of q, k, v, o and dO.  lse, dq,
+ *     dk, dv are always float32.  Arithmetic: products accumulate in fp32 on
+ *     the matrix cores (fp32 inputs use fp32 MFMA; fp16/bf16 inputs use
+ *     fp16/bf16 MFMA with fp32 accumulation); softmax statistics are fp32.
+ *   - `scale` multiplies the scores (1/sqrt(d) is the usual value); gradients
+ *     are with respect to the unscaled q, k, v.
+ *   - `causal` != 0 excludes keys j > i.  `block_mask` (device pointer, may be
+ *     NULL = dense) is uint8 [ceil(N/128)][ceil(N/128)], row-major, one entry
+ *     per 128 x 128 (query tile, key tile) pair, shared by every (b, h); a zero
+ *     entry excludes the whole tile.  causal and block_mask combine with AND.
+ *   - A query row with no visible key gets o = 0, lse = -inf and contributes
+ *     nothing to any gradient.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue work and return without synchronising.
+ *   - Arguments are validated before anything is launched; on any error
+ *     nothing is enqueued and the output buffers are untouched.  There is no
+ *     fallback path: an unsupported shape or dtype is an error.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, B/H/N < 1, bad dtype, non-finite scale */
+  FA_ERR_UNSUPPORTED = -2, /* valid request this build does not implement (e.g. d not 64/128) */
+  FA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than fa_backward_workspace_size() */
+  FA_ERR_HIP = -4          /* the HIP runtime reported an error at launch */
+} fa_status;
+
+#define FA_MASK_BLOCK 128
+
+/*
+ * Forward pass.  Writes o (B,H,N,d; dtype) and lse (B,H,N; fp32), where
+ *   lse_i = m_i + ln(l_i),  m_i = max_j s_ij,  l_i = sum_j exp(s_ij - m_i),
+ * over the visible keys j of query i, s_ij = scale * <q_i, k_j> (natural log).
+ * Supported: d in {64, 128}; dtype FA_F32, FA_F16, FA_BF16.
+ */
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal,
+               const uint8_t* block_mask, int dtype, void* stream);
+
+/* Bytes of device workspace fa_backward needs for this shape (0 on bad input). */
+size_t fa_backward_workspace_size(int B, int H, int N, int d);
+
+/*
+ * Backward pass of L with upstream gradient dO = dL/dO.  Inputs: q, k, v, the
+ * forward's o and lse, dO (dtype).  Outputs (fp32, B,H,N,d, fully overwritten):
+ *   dv = P^T dO,  dq = scale * dS K,  dk = scale * dS^T Q,
+ *   P_ij = exp(s_ij - lse_i) on visible keys (else 0),
+ *   dS = P o (dP - D),  dP = dO V^T,  D_i = sum_c dO_ic * o_ic.
+ * `workspace` is a device buffer of at least fa_backward_workspace_size() bytes,
+ * owned by the caller, scratch for the duration of the call.
+ * Supported: d in {64, 128}; dtype FA_F16, FA_BF16 (FA_F32 -> FA_ERR_UNSUPPORTED).
+ */
+int fa_backward(const void* q, const void* k, const void* v, const void* o,
+                const void* dO, const float* lse,
+                float* dq, float* dk, float* dv,
+                int B, int H, int N, int d, float scale, int causal,
+                const uint8_t* block_mask, int dtype,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable text for a status code. */
+const char* fa_status_string(int status);
+
+/* Library ABI version (this header: 1). */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

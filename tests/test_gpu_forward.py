@@ -1,0 +1,118 @@
+"""GPU parity of the forward pass against the fp64 oracle (through the C ABI).
+
+Small cases span several query/key tiles and ragged tails, where the oracle
+runs every element; the named workloads run at full size in the launch
+configuration the benchmark times, compared on every head the oracle can
+afford plus sampled rows of every other head.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from exact_io_aware_34_amd import workloads as W
+from tests.parity import (DT, LSE_TOL, TOL, assert_close, f64, oracle_forward_heads,
+                          random_block_mask)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    from exact_io_aware_34_amd import fa as _fa
+    return _fa
+
+
+def run_fwd(fa, q, k, v, scale, causal, mask):
+    dev = "cuda"
+    qd, kd, vd = (t.to(dev).contiguous() for t in (q, k, v))
+    md = None if mask is None else mask.to(dev)
+    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale, block_mask=md)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+SMALL = [
+    # B, H, N, d, dtype, causal, sparse
+    (1, 1, 1, 64, "bf16", False, False),
+    (1, 1, 1, 64, "bf16", True, False),
+    (1, 2, 7, 64, "f16", True, False),
+    (2, 2, 128, 64, "bf16", False, False),
+    (1, 3, 300, 64, "bf16", True, False),
+    (1, 2, 300, 64, "f16", False, False),
+    (2, 1, 1000, 64, "bf16", True, False),
+    (1, 2, 1000, 64, "bf16", False, True),
+    (1, 2, 1000, 64, "f16", True, True),
+    (1, 2, 257, 128, "bf16", False, False),
+    (1, 2, 700, 128, "bf16", True, False),
+    (1, 2, 700, 128, "f16", False, True),
+    (1, 1, 1, 64, "f32", False, False),
+    (1, 2, 300, 64, "f32", False, False),
+    (1, 2, 300, 64, "f32", True, False),
+    (1, 1, 600, 64, "f32", True, True),
+    (1, 1, 333, 128, "f32", False, False),
+    (1, 1, 333, 128, "f32", True, True),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype,causal,sparse", SMALL)
+def test_forward_small(fa, B, H, N, d, dtype, causal, sparse):
+    q, k, v, _ = W.draw_qkvdo(B, H, N, d, dtype, seed=N * 7 + d, with_do=False) + ()
+    mask = random_block_mask(N, 0.4, seed=N) if sparse else None
+    scale = W.scale_for(d)
+    o, lse = run_fwd(fa, q, k, v, scale, causal, mask)
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    ref = oracle_forward_heads(q, k, v, scale, causal, mask, heads)
+    for (b, h), (ro, rl) in zip(heads, ref):
+        assert_close(f"o[{b},{h}]", f64(o[b, h]), ro, TOL[DT[dtype]])
+        assert_close(f"lse[{b},{h}]", f64(lse[b, h]), rl, LSE_TOL)
+
+
+def test_forward_is_deterministic(fa):
+    q, k, v, _ = W.draw_qkvdo(1, 4, 1000, 64, "bf16", seed=3, with_do=False) + ()
+    a = run_fwd(fa, q, k, v, 0.125, True, None)
+    b = run_fwd(fa, q, k, v, 0.125, True, None)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("name", ["dense_n256_d64_f32", "dense_n4096_d64_f32",
+                                  "dense_n4096_d64_bf16"])
+def test_forward_named_small_workloads(fa, name):
+    w = W.make(name)
+    o, lse = run_fwd(fa, w["q"], w["k"], w["v"], w["scale"], w["causal"], w["mask"])
+    (ro, rl), = oracle_forward_heads(w["q"], w["k"], w["v"], w["scale"], w["causal"],
+                                     w["mask"], [(0, 0)])
+    tol = TOL[w["q"].dtype]
+    assert_close("o", f64(o[0, 0]), ro, tol)
+    assert_close("lse", f64(lse[0, 0]), rl, LSE_TOL)
+
+
+LARGE = {
+    # workload: (heads checked on every row, number of sampled rows on the others)
+    "causal_b4h12_n8192_d64_bf16": ([(0, 0), (3, 11)], 24),
+    "causal_b1h12_n23400_d64_f16": ([(0, 5)], 24),
+    "sparse_b2h16_n16384_d128_bf16": ([(1, 15)], 16),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LARGE))
+def test_forward_named_large_workloads(fa, name):
+    w = W.make(name)
+    wl = w["workload"]
+    o, lse = run_fwd(fa, w["q"], w["k"], w["v"], w["scale"], w["causal"], w["mask"])
+    tol = TOL[w["q"].dtype]
+    full_heads, n_rows = LARGE[name]
+    for (b, h), (ro, rl) in zip(full_heads, oracle_forward_heads(
+            w["q"], w["k"], w["v"], w["scale"], w["causal"], w["mask"], full_heads)):
+        assert_close(f"o[{b},{h}]", f64(o[b, h]), ro, tol)
+        assert_close(f"lse[{b},{h}]", f64(lse[b, h]), rl, LSE_TOL)
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, wl.N - 1],
+                                     rng.integers(0, wl.N, n_rows)]))
+    others = [(b, h) for b in range(wl.B) for h in range(wl.H) if (b, h) not in full_heads]
+    sampled = oracle_forward_heads(w["q"], w["k"], w["v"], w["scale"], w["causal"],
+                                   w["mask"], others, rows=rows)
+    for (b, h), (ro, rl) in zip(others, sampled):
+        assert_close(f"o[{b},{h}] rows", f64(o[b, h][rows]), ro, tol)
+        assert_close(f"lse[{b},{h}] rows", f64(lse[b, h][rows]), rl, LSE_TOL)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
