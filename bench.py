@@ -1,0 +1,172 @@
+"""Throughput of exact attention forward + backward on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one forward pass and one backward pass (every kernel of the path:
+forward, backward preprocess, backward main) over the workload's synthetic
+inputs, which are resident in HBM before the timed region starts.  FLOPs are
+counted as 4*N^2*d per head for the forward and 10*N^2*d per head for the
+backward, halved for causal masking and scaled by the fraction of 128x128
+tiles the block mask keeps.  One JSON line is printed.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X dense, published
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention fwd/bwd TFLOPS (bf16, N=8192, d=64, causal) and % of MFMA peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=4,
+                    help="heads of the workload the oracle is timed on")
+    return ap.parse_args()
+
+
+def work_fraction(w, mask):
+    """Fraction of the dense N^2 score matrix the method evaluates."""
+    frac = 0.5 if w.causal else 1.0
+    if mask is not None:
+        frac *= float(mask.float().mean())
+    return frac
+
+
+def flops(w, mask):
+    f = work_fraction(w, mask) * w.N * w.N * w.d * w.B * w.H
+    return 4.0 * f, 10.0 * f
+
+
+def cpu_baseline(w, inputs, n_heads):
+    """Time the fp64 oracle on `n_heads` heads of the same workload (fwd+bwd)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    mask = None if inputs["mask"] is None else inputs["mask"].numpy()
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)][:n_heads]
+    t0 = time.perf_counter()
+    for b, h in heads:
+        a = [inputs[n][b, h].double().numpy() for n in ("q", "k", "v")]
+        oracle.forward_head(*a, w.scale, causal=w.causal, block_mask=mask)
+        if w.backward:
+            oracle.backward_head(*a, inputs["do"][b, h].double().numpy(), w.scale,
+                                 causal=w.causal, block_mask=mask)
+    dt = time.perf_counter() - t0
+    f_fwd, f_bwd = flops(w, inputs["mask"])
+    per_head = (f_fwd + (f_bwd if w.backward else 0.0)) / (w.B * w.H)
+    threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    return {"value": per_head * len(heads) / dt / 1e12, "unit": "TFLOPS", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"{len(heads)} of {w.B * w.H} heads, forward"
+                      f"{' + backward' if w.backward else ''}, numpy float64, "
+                      f"os.cpu_count()={os.cpu_count()}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards over independent (batch, head) pairs; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from exact_io_aware_34_amd import build as _build
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    from exact_io_aware_34_amd import fa
+    from exact_io_aware_34_amd import workloads as W
+
+    name = args.workload or W.HEADLINE
+    w = W.WORKLOADS[name]
+    inputs = W.make(name)
+    dev = torch.device("cuda:0")
+    q, k, v = (inputs[n].to(dev) for n in ("q", "k", "v"))
+    do = inputs["do"].to(dev) if w.backward else None
+    mask = None if inputs["mask"] is None else inputs["mask"].to(dev)
+    B, H, N, d = w.B, w.H, w.N, w.d
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    grads = tuple(torch.empty((B, H, N, d), dtype=torch.float32, device=dev) for _ in range(3))
+    ws = torch.empty(fa.workspace_size(B, H, N, d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.forward(q, k, v, causal=w.causal, scale=w.scale, block_mask=mask, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record(stream)
+        if w.backward:
+            fa.backward(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, block_mask=mask,
+                        workspace=ws, grads=grads)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in events] if w.backward else [0.0]
+    mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
+    f_fwd, f_bwd = flops(w, mask.cpu() if mask is not None else None)
+    if not w.backward:
+        f_bwd = 0.0
+    ms_step = wall * 1e3 / args.steps
+    value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    fwd_tf = f_fwd / (mean(fwd_ms) * 1e-3) / 1e12
+    bwd_tf = f_bwd / (mean(bwd_ms) * 1e-3) / 1e12 if w.backward else None
+
+    # Dominant kernel by time: the backward call (bwd_pre + bwd_main) when present.
+    if w.backward and mean(bwd_ms) >= mean(fwd_ms):
+        dom, dom_ms, dom_flops = "fa_backward (bwd_pre + bwd_dkdv + bwd_dq)", mean(bwd_ms), f_bwd
+    else:
+        dom, dom_ms, dom_flops = "fa_forward (fwd16_kernel)", mean(fwd_ms), f_fwd
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "avg_ms": round(dom_ms, 4)}
+
+    out = {
+        "metric": METRIC if name == W.HEADLINE else f"attention TFLOPS ({name})",
+        "value": round(value, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
+                   "block_sparse": w.sparse, "passes": "fwd+bwd" if w.backward else "fwd",
+                   "work_fraction": round(work_fraction(w, inputs["mask"]), 5)},
+        "fwd_ms": round(mean(fwd_ms), 4), "bwd_ms": round(mean(bwd_ms), 4),
+        "fwd_tflops": round(fwd_tf, 2), "fwd_frac_peak": round(fwd_tf / peak, 4),
+        "bwd_tflops": None if bwd_tf is None else round(bwd_tf, 2),
+        "bwd_frac_peak": None if bwd_tf is None else round(bwd_tf / peak, 4),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_heads)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

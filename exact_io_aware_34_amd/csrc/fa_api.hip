@@ -16,7 +16,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 int check_common(int B, int H, int N, int d, float scale, int dtype) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
-  if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   // Grid sizes and per-head element counts must fit the kernels' int indexing.
   const long long bh = (long long)B * H;
@@ -41,7 +41,7 @@ int fa_abi_version(void) { return 1; }
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
-    case FA_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad size, dtype or scale)";
+    case FA_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad size or dtype, scale not finite and > 0)";
     case FA_ERR_UNSUPPORTED: return "unsupported request (head dim must be 64 or 128; size limits; dtype)";
     case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_backward_workspace_size()";
     case FA_ERR_HIP: return "HIP runtime error at kernel launch";
@@ -69,6 +69,7 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
   p.mask_tiles = (N + fa::MASK_TILE - 1) / fa::MASK_TILE;
   p.scale = scale;
   p.scale_log2e = scale * kLog2e;
+  p.rescale_thr = 8.0f / p.scale_log2e;  // 2^8 headroom for the exponentials
   const hipError_t e = fa::launch_forward(p, dtype, d, causal != 0, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

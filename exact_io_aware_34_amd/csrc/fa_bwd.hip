@@ -8,19 +8,25 @@
 //   P = exp(scale*QK^T - lse),  dV = P^T dO,  dP = dO V^T,
 //   D_i = sum_c dO_ic O_ic,  dS = P o (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
 //
-// Kernels:
-//   bwd_pre:  D = rowsum(dO o O) in fp32 into the workspace, and dq := 0.
-//   bwd_main: one workgroup per (key tile of 128, batch*head); wave w owns 32
-//     keys, keeps its K and V rows in VGPRs and its dK, dV in fp32
-//     accumulators, and loops over the query tiles of 32 rows that can see
-//     them (causal: query tiles at or after the key tile; block-sparse: mask
-//     entries that are set).  Per query tile:
-//       S = Q K^T and dP = dO V^T on v_mfma_f32_32x32x16 (lane = key, so the
-//       P^T and dS^T operands of dV += P^T dO and dK += dS^T Q come straight
-//       from the accumulators; dO and Q are read with ds_read_b64_tr_b16),
-//       dS^T of all four waves is staged in LDS, and dQ_tile += scale dS K is
-//       computed on v_mfma_f32_16x16x32 split over the waves and added to the
-//       fp32 dq with global atomics.
+// Three kernels, no atomics:
+//   bwd_pre:  D = rowsum(dO o O) in fp32 (the workspace).
+//   bwd_dkdv: one workgroup per (key tile of 128, batch*head).  Wave w owns 32
+//     keys, keeps their K and V rows in VGPRs and dK, dV in fp32
+//     accumulators, and loops over the 32-row query tiles that can see them
+//     (causal: tiles at or after the key tile; block-sparse: set entries).
+//     S = Q K^T and dP = dO V^T run on v_mfma_f32_32x32x16 with the key in
+//     the lane, so P^T and dS^T for dV += P^T dO and dK += dS^T Q come
+//     straight from the accumulators; dO and Q are read with
+//     ds_read_b64_tr_b16.  Q, dO, lse and D tiles are double buffered in
+//     LDS with one barrier per query tile.
+//   bwd_dq: one workgroup per (query tile of 128, batch*head), the forward's
+//     schedule: S^T = K Q^T and dP^T = V dO^T with the query in the lane (so
+//     lse and D are per-lane scalars), dS^T in registers, and
+//     dQ^T += K^T dS^T with K read by ds_read_b64_tr_b16; dQ stays in
+//     registers and is stored once.
+// Recomputing S, P, dP in both kernels costs two extra products per score,
+// instead of the global atomic adds a single-pass dQ would need (those go to
+// memory on this part and moved more bytes than the whole pass computes).
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -28,10 +34,11 @@ namespace fa {
 
 namespace {
 
+constexpr float kLog2e = 1.4426950408889634f;
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO,
-                                                      float* __restrict__ delta, float* __restrict__ dq,
-                                                      size_t rows) {
+                                                      float* __restrict__ delta, size_t rows) {
   using VT = typename V8<T>::t;
   constexpr int LPR = D / 8;  // lanes per row, 8 elements each
   const size_t gt = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -43,28 +50,24 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, c
     const VT b = *(const VT*)(dO + row * D + part * 8);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
-    float4* z = (float4*)(dq + row * D + part * 8);
-    z[0] = make_float4(0.f, 0.f, 0.f, 0.f);
-    z[1] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (row < rows && part == 0) delta[row] = acc;
 }
 
+// log2-domain row statistic: +inf makes P = 0 for padding rows and for rows
+// with no visible key (lse = -inf).
+__device__ __forceinline__ float lse_log2(float l) { return l == -INFINITY ? INFINITY : l * kLog2e; }
+
 template <typename T, int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
   using VT = typename V8<T>::t;
-  using HT = typename V8<T>::h;
-  constexpr int BC = 128, QB = 32, RS = D + 8, RST = QB + 8;
+  constexpr int BC = 128, QB = 32, RS = D + 8;
   constexpr int DS = D / 16, DB = D / 32;
-  constexpr int CPR = D / 8, PTQ = QB * D / 8 / 256, PTK = BC * D / 8 / 256;
-  constexpr int NQB16 = QB / 16, NDB16 = D / 16, DQ_PER_WAVE = NQB16 * NDB16 / 4;
-  constexpr float LOG2E = 1.4426950408889634f;
+  constexpr int CPR = D / 8, PTQ = QB * D / 8 / 256;
   __shared__ __attribute__((aligned(16))) T qs[2][QB * RS];
   __shared__ __attribute__((aligned(16))) T dos[2][QB * RS];
-  __shared__ __attribute__((aligned(16))) T kls[BC * RS];
-  __shared__ __attribute__((aligned(16))) T dst[BC * RST];
   __shared__ __attribute__((aligned(16))) float lsel[2][QB];
   __shared__ __attribute__((aligned(16))) float dls[2][QB];
 
@@ -82,7 +85,6 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
   const T* __restrict__ dO = (const T*)p.dO + base;
   const float* __restrict__ LSE = p.lse + (size_t)bh * N;
   const float* __restrict__ DEL = p.delta + (size_t)bh * N;
-  float* __restrict__ dQ = p.dq + base;
   const int k0 = j * BC, kw0 = k0 + 32 * wave, my_k = kw0 + l32;
   const float c = p.scale_log2e;
 
@@ -96,12 +98,6 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
       kf[ds] = VT{};
       vf[ds] = VT{};
     }
-  }
-#pragma unroll
-  for (int u = 0; u < PTK; ++u) {
-    const int cc = tid + 256 * u, row = cc / CPR, col = (cc % CPR) * 8;
-    const int key = k0 + row;
-    *(VT*)(&kls[row * RS + col]) = key < N ? *(const VT*)(K + (size_t)key * D + col) : VT{};
   }
 
   f32x16 dk[DB], dv[DB];
@@ -136,10 +132,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
     }
     if (tid < QB) {
       const int q = i * QB + tid;
-      // log2-domain statistic; +inf makes P = 0 for padding rows and for
-      // rows with no visible key (lse = -inf).
-      const float l = q < N ? LSE[q] : -INFINITY;
-      lreg = l == -INFINITY ? INFINITY : l * LOG2E;
+      lreg = lse_log2(q < N ? LSE[q] : -INFINITY);
       dreg = q < N ? DEL[q] : 0.f;
     }
   };
@@ -167,7 +160,6 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
     const int in = next_active(i + 1);
     if (in < i_end) gload(in);
     const int qa = i * QB;
-    T* dsrow = &dst[(32 * wave + l32) * RST];
     if (!CAUSAL || qa + QB - 1 >= kw0) {
       f32x16 s = f32x16{}, dp = f32x16{};
       const T* qb_ = qs[buf];
@@ -179,30 +171,34 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
         const VT da_ = *(const VT*)(&db_[l32 * RS + 16 * ds + 8 * g]);
         dp = mfma32x32x16(da_, vf[ds], dp);
       }
-      // lane: key my_k; register r: query qa + 8*(r/4) + 4*g + r%4
+      // Lane: key my_k; register r: query qa + 8*(r/4) + 4*g + r%4.
       const bool need_mask = (kw0 + 32 > N) || (CAUSAL && qa < kw0 + 31);
-      VT pa[2], dsa[2];
+      // Visible iff query offset (within the tile) >= lim (causal) and key < N.
+      const int lim = (my_k >= N) ? (1 << 30) : (CAUSAL ? my_k - qa - 4 * g : -(1 << 30));
+      VT pa[2] = {VT{}, VT{}}, dsa[2] = {VT{}, VT{}};
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const float4 l4 = *(const float4*)(&lsel[buf][8 * rg + 4 * g]);
         const float4 d4 = *(const float4*)(&dls[buf][8 * rg + 4 * g]);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
         const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-        HT hs;
+        float pv[4], dsv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * rg + e;
-          float pv = fast_exp2(fmaf(s[r], c, -lv[e]));
-          if (need_mask) {
-            const int qi = qa + 8 * rg + 4 * g + e;
-            if (my_k >= N || (CAUSAL && my_k > qi)) pv = 0.f;
-          }
-          const float dsv = pv * (dp[r] - dv4[e]);
-          pa[r >> 3][r & 7] = (T)pv;
-          dsa[r >> 3][r & 7] = (T)dsv;
-          hs[e] = (T)dsv;
+          pv[e] = fast_exp2(fmaf(s[r], c, -lv[e]));
+          if (need_mask && 8 * rg + e < lim) pv[e] = 0.f;
+          dsv[e] = pv[e] * (dp[r] - dv4[e]);
         }
-        *(HT*)(dsrow + 8 * rg + 4 * g) = hs;
+        const int kk = rg >> 1, w0 = 2 * (rg & 1);
+        u32x4 pw = __builtin_bit_cast(u32x4, pa[kk]);
+        u32x4 dw = __builtin_bit_cast(u32x4, dsa[kk]);
+        pw[w0] = pack2<T>(pv[0], pv[1]);
+        pw[w0 + 1] = pack2<T>(pv[2], pv[3]);
+        dw[w0] = pack2<T>(dsv[0], dsv[1]);
+        dw[w0 + 1] = pack2<T>(dsv[2], dsv[3]);
+        pa[kk] = __builtin_bit_cast(VT, pw);
+        dsa[kk] = __builtin_bit_cast(VT, dw);
       }
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -217,31 +213,6 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
                                      lds_read_tr16(&qb_[(row + 8) * RS + col]));
           dk[db] = mfma32x32x16(dsa[kk], qf, dk[db]);
         }
-    } else {
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) *(HT*)(dsrow + 8 * rg + 4 * g) = HT{};
-    }
-    __syncthreads();
-    // dQ[qa .. qa+31][:] += scale * dS K over this tile's 128 keys.
-#pragma unroll
-    for (int t = 0; t < DQ_PER_WAVE; ++t) {
-      const int b = wave * DQ_PER_WAVE + t;
-      const int qb = b / NDB16, dbk = b % NDB16;
-      f32x4 acc = f32x4{};
-#pragma unroll
-      for (int ks = 0; ks < BC / 32; ++ks) {
-        const int kb = 32 * ks + 8 * gq + (s16 >> 2);
-        const VT af = cat_tr16<VT>(lds_read_tr16(&dst[kb * RST + 16 * qb + 4 * (s16 & 3)]),
-                                   lds_read_tr16(&dst[(kb + 4) * RST + 16 * qb + 4 * (s16 & 3)]));
-        const VT bf = cat_tr16<VT>(lds_read_tr16(&kls[kb * RS + 16 * dbk + 4 * (s16 & 3)]),
-                                   lds_read_tr16(&kls[(kb + 4) * RS + 16 * dbk + 4 * (s16 & 3)]));
-        acc = mfma16x16x32(af, bf, acc);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int q = qa + 16 * qb + 4 * gq + r;
-        if (q < N) unsafeAtomicAdd(&dQ[(size_t)q * D + 16 * dbk + s16], acc[r] * p.scale);
-      }
     }
     if (in < i_end) lstore(buf ^ 1);
     __syncthreads();
@@ -264,20 +235,188 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
     }
 }
 
-template <typename T, int D>
-hipError_t launch_bwd(const BwdParams& p, bool causal, bool sparse, hipStream_t st) {
+template <typename T, int D, bool CAUSAL, bool SPARSE>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
+  using VT = typename V8<T>::t;
+  constexpr int BR = 128, BC = 64, RS = D + 8;
+  constexpr int DS = D / 16, DB = D / 32;
+  constexpr int CPR = D / 8, PT = BC * D / 8 / 256;
+  __shared__ __attribute__((aligned(16))) T ks[2][BC * RS];
+  __shared__ __attribute__((aligned(16))) T vs[2][BC * RS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31, s16 = lane & 15, gq = lane >> 4;
+  const int N = p.N;
+  const int n_qt = (N + BR - 1) / BR;
+  const int total = n_qt * p.BH;
+  const int lid = xcd_remap(blockIdx.x, total);
+  const int bh = lid / n_qt;
+  const int ir = lid - bh * n_qt;
+  const int qt = CAUSAL ? (n_qt - 1 - ir) : ir;
+  const size_t base = (size_t)bh * N * D;
+  const T* __restrict__ Q = (const T*)p.q + base;
+  const T* __restrict__ K = (const T*)p.k + base;
+  const T* __restrict__ V = (const T*)p.v + base;
+  const T* __restrict__ dO = (const T*)p.dO + base;
+  const int q0 = qt * BR + wave * 32;
+  const int my_q = q0 + l32;
+  const float c = p.scale_log2e;
+
+  VT qf[DS], dof[DS];
+  float lq = INFINITY, dq_row = 0.f;
+  if (my_q < N) {
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      qf[ds] = *(const VT*)(Q + (size_t)my_q * D + 16 * ds + 8 * g);
+      dof[ds] = *(const VT*)(dO + (size_t)my_q * D + 16 * ds + 8 * g);
+    }
+    lq = lse_log2(p.lse[(size_t)bh * N + my_q]);
+    dq_row = p.delta[(size_t)bh * N + my_q];
+  } else {
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      qf[ds] = VT{};
+      dof[ds] = VT{};
+    }
+  }
+
+  const int n_kt = (N + BC - 1) / BC;
+  int kt_end = n_kt;
+  if (CAUSAL) kt_end = min(kt_end, (min(N, (qt + 1) * BR) + BC - 1) / BC);
+  const uint8_t* mrow = SPARSE ? p.mask + (size_t)qt * p.mask_tiles : nullptr;
+  auto next_active = [&](int jj) {
+    if (SPARSE)
+      while (jj < kt_end && mrow[(jj * BC) / MASK_TILE] == 0) ++jj;
+    return jj;
+  };
+
+  VT kreg[PT], vreg[PT];
+  auto gload = [&](int jj) {
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int cc = tid + 256 * u, row = cc / CPR, col = (cc % CPR) * 8;
+      const int key = jj * BC + row;
+      if (key < N) {
+        kreg[u] = *(const VT*)(K + (size_t)key * D + col);
+        vreg[u] = *(const VT*)(V + (size_t)key * D + col);
+      } else {
+        kreg[u] = VT{};
+        vreg[u] = VT{};
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int cc = tid + 256 * u, row = cc / CPR, col = (cc % CPR) * 8;
+      *(VT*)(&ks[buf][row * RS + col]) = kreg[u];
+      *(VT*)(&vs[buf][row * RS + col]) = vreg[u];
+    }
+  };
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+
+  int jj = next_active(0);
+  if (jj < kt_end) {
+    gload(jj);
+    lstore(0);
+  }
+  __syncthreads();
+  int buf = 0;
+  while (jj < kt_end) {
+    const int jn = next_active(jj + 1);
+    if (jn < kt_end) gload(jn);
+    const int k0 = jj * BC;
+    if (!CAUSAL || k0 <= q0 + 31) {
+      f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+      const T* kb_ = ks[buf];
+      const T* vb_ = vs[buf];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) {
+          const VT kfr = *(const VT*)(&kb_[(32 * kb + l32) * RS + 16 * ds + 8 * g]);
+          s[kb] = mfma32x32x16(kfr, qf[ds], s[kb]);
+          const VT vfr = *(const VT*)(&vb_[(32 * kb + l32) * RS + 16 * ds + 8 * g]);
+          dp[kb] = mfma32x32x16(vfr, dof[ds], dp[kb]);
+        }
+      const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0);
+      int lim = N - 1 - k0;
+      if (CAUSAL) lim = min(lim, my_q - k0);
+      lim -= 4 * g;
+      VT dsf[4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          u32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float dsv[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const int r = 8 * h + 2 * e + t;
+              float pv = fast_exp2(fmaf(s[kb][r], c, -lq));
+              if (need_mask && 32 * kb + 8 * (r >> 2) + (r & 3) > lim) pv = 0.f;
+              dsv[t] = pv * (dp[kb][r] - dq_row);
+            }
+            w[e] = pack2<T>(dsv[0], dsv[1]);
+          }
+          dsf[2 * kb + h] = __builtin_bit_cast(VT, w);
+        }
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int row = 16 * kk + 4 * g + (s16 >> 2);
+          const int col = 32 * db + 16 * (gq & 1) + 4 * (s16 & 3);
+          const VT kt = cat_tr16<VT>(lds_read_tr16(&kb_[row * RS + col]),
+                                     lds_read_tr16(&kb_[(row + 8) * RS + col]));
+          acc[db] = mfma32x32x16(kt, dsf[kk], acc[db]);
+        }
+    }
+    if (jn < kt_end) lstore(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    jj = jn;
+  }
+
+  // dQ = scale * dS K; lane: query my_q, register r: column 8*(r/4)+4*g+r%4.
+  if (my_q < N) {
+    float* __restrict__ row = p.dq + base + (size_t)my_q * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg)
+        *(float4*)(row + 32 * db + 8 * rg + 4 * g) =
+            make_float4(acc[db][4 * rg] * p.scale, acc[db][4 * rg + 1] * p.scale,
+                        acc[db][4 * rg + 2] * p.scale, acc[db][4 * rg + 3] * p.scale);
+  }
+}
+
+template <typename T, int D, bool CAUSAL, bool SPARSE>
+hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
   const size_t rows = (size_t)p.BH * p.N;
   const size_t threads = rows * (D / 8);
   bwd_pre_kernel<T, D><<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st>>>(
-      (const T*)p.o, (const T*)p.dO, p.delta, p.dq, rows);
+      (const T*)p.o, (const T*)p.dO, p.delta, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 grid(p.n_ktiles * p.BH), block(256);
-  if (causal && sparse) bwd_main_kernel<T, D, true, true><<<grid, block, 0, st>>>(p);
-  else if (causal) bwd_main_kernel<T, D, true, false><<<grid, block, 0, st>>>(p);
-  else if (sparse) bwd_main_kernel<T, D, false, true><<<grid, block, 0, st>>>(p);
-  else bwd_main_kernel<T, D, false, false><<<grid, block, 0, st>>>(p);
+  bwd_dkdv_kernel<T, D, CAUSAL, SPARSE><<<dim3(p.n_ktiles * p.BH), dim3(256), 0, st>>>(p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  bwd_dq_kernel<T, D, CAUSAL, SPARSE><<<dim3(((p.N + 127) / 128) * p.BH), dim3(256), 0, st>>>(p);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_bwd(const BwdParams& p, bool causal, bool sparse, hipStream_t st) {
+  if (causal && sparse) return launch_bwd_t<T, D, true, true>(p, st);
+  if (causal) return launch_bwd_t<T, D, true, false>(p, st);
+  if (sparse) return launch_bwd_t<T, D, false, true>(p, st);
+  return launch_bwd_t<T, D, false, false>(p, st);
 }
 
 }  // namespace

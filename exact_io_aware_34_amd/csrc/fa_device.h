@@ -39,9 +39,33 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
 template <typename T> struct V8;
-template <> struct V8<__bf16> { typedef bf16x8 t; typedef bf16x4 h; };
-template <> struct V8<_Float16> { typedef f16x8 t; typedef f16x4 h; };
+template <> struct V8<__bf16> { typedef bf16x8 t; typedef bf16x4 h; typedef bf16x2 p; };
+template <> struct V8<_Float16> { typedef f16x8 t; typedef f16x4 h; typedef f16x2 p; };
+
+// Round two fp32 values to one packed pair (round to nearest even).
+template <typename T>
+__device__ __forceinline__ unsigned pack2(float a, float b) {
+  typename V8<T>::p v = {(T)a, (T)b};
+  return __builtin_bit_cast(unsigned, v);
+}
+
+// acc + x.lo + x.hi for a packed pair, accumulated in fp32.
+__device__ __forceinline__ float sum2_acc(unsigned x, float acc, __bf16) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), one, acc, false);
+}
+__device__ __forceinline__ float sum2_acc(unsigned x, float acc, _Float16) {
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), one, acc, false);
+}
+
+// True if `pred` holds on any active lane of the wave.
+__device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
 
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);

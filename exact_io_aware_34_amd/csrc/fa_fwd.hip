@@ -130,36 +130,57 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdParams p) {
         }
       const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0);
       if (need_mask) {
+        // Key offset (within the tile) of the last visible key for this
+        // lane's query, less the lane's 4*g row offset in the accumulator.
+        int lim = N - 1 - k0;
+        if (CAUSAL) lim = min(lim, my_q - k0);
+        lim -= 4 * g;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key >= N || (CAUSAL && key > my_q)) s[kb][r] = -INFINITY;
-          }
+          for (int r = 0; r < 16; ++r)
+            if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
       }
-      float mx = m_run;
+      float mx = s[0][0];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
       mx = half_swap_max(mx);
-      const float alpha = fast_exp2((m_run - mx) * c);
-      m_run = mx;
-      const float mc = mx * c;
+      // Lazy rescale: the running max only moves when some row's tile max
+      // exceeds it by more than 8 in log2 units, so the exponentials stay
+      // <= 2^8 and O, l are rescaled rarely.  Any reference value gives the
+      // same O and lse as long as O, l and lse share it.
+      if (wave_any(mx > m_run + p.rescale_thr)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2((m_run - m_new) * c);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      }
+      const float mc = m_run * c;
+      // Row sums stay in fp32 on the unrounded exponentials (the saved lse
+      // depends on them); only the PV operand is rounded to 16 bits.
       VT pf[4];
-      float ls = 0.f;
+      float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(fmaf(s[kb][r], c, -mc));
-          ls += e;
-          pf[2 * kb + (r >> 3)][r & 7] = (T)e;
-        }
-      l_run = l_run * alpha + ls;
+        for (int h = 0; h < 2; ++h) {
+          u32x4 w;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+          for (int e = 0; e < 4; ++e) {
+            const int r = 8 * h + 2 * e;
+            const float e0 = fast_exp2(fmaf(s[kb][r], c, -mc));
+            const float e1 = fast_exp2(fmaf(s[kb][r + 1], c, -mc));
+            ls0 += e0;
+            ls1 += e1;
+            w[e] = pack2<T>(e0, e1);
+          }
+          pf[2 * kb + h] = __builtin_bit_cast(VT, w);
+        }
+      l_run += ls0 + ls1;
       const T* vb = vs[buf];
 #pragma unroll
       for (int db = 0; db < DB; ++db)

@@ -21,6 +21,7 @@ struct FwdParams {
   int BH, N;
   int n_qtiles, n_ktiles, mask_tiles;
   float scale, scale_log2e;
+  float rescale_thr;  // raw-score growth of the running max that forces a rescale
 };
 
 struct BwdParams {

@@ -28,8 +28,8 @@
  *     dk, dv are always float32.  Arithmetic: products accumulate in fp32 on
  *     the matrix cores (fp32 inputs use fp32 MFMA; fp16/bf16 inputs use
  *     fp16/bf16 MFMA with fp32 accumulation); softmax statistics are fp32.
- *   - `scale` multiplies the scores (1/sqrt(d) is the usual value); gradients
- *     are with respect to the unscaled q, k, v.
+ *   - `scale` (finite, > 0) multiplies the scores (1/sqrt(d) is the usual
+ *     value); gradients are with respect to the unscaled q, k, v.
  *   - `causal` != 0 excludes keys j > i.  `block_mask` (device pointer, may be
  *     NULL = dense) is uint8 [ceil(N/128)][ceil(N/128)], row-major, one entry
  *     per 128 x 128 (query tile, key tile) pair, shared by every (b, h); a zero
@@ -56,7 +56,7 @@ typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
 
 typedef enum {
   FA_OK = 0,
-  FA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, B/H/N < 1, bad dtype, non-finite scale */
+  FA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, B/H/N < 1, bad dtype, scale not finite > 0 */
   FA_ERR_UNSUPPORTED = -2, /* valid request this build does not implement (e.g. d not 64/128) */
   FA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than fa_backward_workspace_size() */
   FA_ERR_HIP = -4          /* the HIP runtime reported an error at launch */

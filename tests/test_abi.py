@@ -79,6 +79,8 @@ def test_forward_validation(lib):
     assert fwd(lib, dtype=3) == -1
     assert fwd(lib, scale=float("nan")) == -1
     assert fwd(lib, scale=float("inf")) == -1
+    assert fwd(lib, scale=0.0) == -1
+    assert fwd(lib, scale=-0.125) == -1
     assert fwd(lib, d=96) == -2
     assert fwd(lib, d=256) == -2
     assert fwd(lib, N=1 << 30, d=64) == -2
