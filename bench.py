@@ -1,6 +1,7 @@
 """Throughput of exact attention forward + backward on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                [--calibrate-copy]
 
 A step is one forward pass and one backward pass (every kernel of the path:
 forward, backward preprocess, backward main) over the workload's synthetic
@@ -8,9 +9,17 @@ inputs, which are resident in HBM before the timed region starts.  FLOPs are
 counted as 4*N^2*d per head for the forward and 10*N^2*d per head for the
 backward, halved for causal masking and scaled by the fraction of 128x128
 tiles the block mask keeps.  One JSON line is printed.
+
+`roofline.traffic` comes from profiles/hbm_traffic_<workload>.json (FETCH_SIZE
+and WRITE_SIZE counter runs of this script, scaled by the same counters on a
+plain device copy of known size, which --calibrate-copy adds before the timed
+steps).  It is reported only while the kernel sources hash to the value
+recorded with those counters; otherwise it is null.
 """
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -33,7 +42,33 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=4,
                     help="heads of the workload the oracle is timed on")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one 1 GiB device-to-device copy before the steps "
+                         "(reference kernel for HBM byte counters)")
     return ap.parse_args()
+
+
+COPY_BYTES = 1 << 30
+
+
+def kernel_sources_sha256():
+    """Hash of the HIP sources the library is built from."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "exact_io_aware_34_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload):
+    """HBM bytes per call from committed counter runs, if they match the sources."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha256") != kernel_sources_sha256():
+        return None
+    return rec
 
 
 def work_fraction(w, mask):
@@ -116,6 +151,12 @@ def main():
         if ev is not None:
             ev[2].record(stream)
 
+    if args.calibrate_copy:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -139,14 +180,18 @@ def main():
     fwd_tf = f_fwd / (mean(fwd_ms) * 1e-3) / 1e12
     bwd_tf = f_bwd / (mean(bwd_ms) * 1e-3) / 1e12 if w.backward else None
 
-    # Dominant kernel by time: the backward call (bwd_pre + bwd_main) when present.
+    # Dominant work by time: the backward call (its kernels run back to back
+    # on the stream, timed together) when present, else the forward kernel.
     if w.backward and mean(bwd_ms) >= mean(fwd_ms):
-        dom, dom_ms, dom_flops = "fa_backward (bwd_pre + bwd_dkdv + bwd_dq)", mean(bwd_ms), f_bwd
+        dom, dom_key, dom_ms, dom_flops = ("fa_backward (bwd_pre + bwd_dkdv + bwd_dq)", "backward",
+                                           mean(bwd_ms), f_bwd)
     else:
-        dom, dom_ms, dom_flops = "fa_forward (fwd16_kernel)", mean(fwd_ms), f_fwd
+        dom, dom_key, dom_ms, dom_flops = "fa_forward (fwd kernel)", "forward", mean(fwd_ms), f_fwd
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    rec = recorded_traffic(name)
+    traffic = None if rec is None else rec["bytes_per_call"].get(dom_key)
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                 "avg_ms": round(dom_ms, 4)}
 
     out = {
