@@ -57,6 +57,8 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
   if (lse == nullptr || !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
   const int rc = check_common(B, H, N, d, scale, dtype);
   if (rc != FA_OK) return rc;
+  if (block_mask != nullptr && (N + fa::MASK_TILE - 1) / fa::MASK_TILE > fa::FWD_MAX_MASK_TILES)
+    return FA_ERR_UNSUPPORTED;
   fa::FwdParams p{};
   p.q = q;
   p.k = k;

@@ -64,6 +64,72 @@ __device__ __forceinline__ float sum2_acc(unsigned x, float acc, _Float16) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), one, acc, false);
 }
 
+// ---- LDS address helpers, direct global->LDS copies and explicit waits ----
+//
+// global_load_lds_dwordx4 copies 16 bytes per lane from global memory into
+// LDS at (M0 + 16 * lane): each wave fills one contiguous 1 KiB block whose
+// base is wave-uniform.  It is issued from inline assembly so that the
+// compiler neither counts it nor inserts its own conservative waits; the
+// kernels wait for it explicitly with s_waitcnt vmcnt(n) (vector-memory
+// operations complete in issue order) and publish it to the other waves with
+// a workgroup barrier.
+
+// Byte address of a __shared__ object as the LDS instructions see it.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p);
+}
+
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_wave_base) {
+  // M0 is an input operand, so the compiler sets it and knows it is used.
+  asm volatile("global_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_wave_base)));
+}
+
+// Same copy with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit
+// byte offset (no per-lane address arithmetic).
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds_wave_base) {
+  asm volatile("global_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "{m0}"(__builtin_amdgcn_readfirstlane(lds_wave_base)));
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// Compiler-visible wait for every outstanding vector-memory load of this
+// wave (vmcnt(0), other counters untouched).  Used once after the prologue's
+// ordinary loads so the compiler's own wait tracking sees them complete and
+// inserts no wait inside the copy-pipelined loop.
+__device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0xF70); }
+
+// Workgroup barrier without the memory fence of __syncthreads(): LDS
+// accesses are not moved across it by the compiler, and no wait on
+// outstanding global loads is added.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" : : : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" : : : "memory");
+}
+
+// XOR swizzle of 16-byte chunks within an LDS row of D 16-bit elements.  For
+// both the 16-byte row reads (16 lanes, 16 consecutive rows, one chunk) and
+// the transpose reads (32 lanes, 4 consecutive rows x 32 columns) every lane
+// of a pass hits a different bank.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  else return ((r & 3) << 2) | ((r >> 2) & 3);
+}
+// Element offset of logical (row, col) in a swizzled tile with rows of D.
+template <int D>
+__device__ __forceinline__ int swz_off(int r, int col) {
+  return r * D + 8 * ((col >> 3) ^ swz<D>(r)) + (col & 7);
+}
+
 // True if `pred` holds on any active lane of the wave.
 __device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
 

@@ -68,7 +68,8 @@ typedef enum {
  * Forward pass.  Writes o (B,H,N,d; dtype) and lse (B,H,N; fp32), where
  *   lse_i = m_i + ln(l_i),  m_i = max_j s_ij,  l_i = sum_j exp(s_ij - m_i),
  * over the visible keys j of query i, s_ij = scale * <q_i, k_j> (natural log).
- * Supported: d in {64, 128}; dtype FA_F32, FA_F16, FA_BF16.
+ * Supported: d in {64, 128}; dtype FA_F32, FA_F16, FA_BF16; with a block_mask,
+ * N <= 262144 (2048 mask tiles).
  */
 int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int N, int d, float scale, int causal,
