@@ -94,6 +94,13 @@ __device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32
                : "v"(voff), "s"(sbase), "{m0}"(__builtin_amdgcn_readfirstlane(lds_wave_base)));
 }
 
+// 4-byte-per-lane variant: lane l's dword lands at lds_wave_base + 4 * l.
+__device__ __forceinline__ void dma4(const void* gsrc, uint32_t lds_wave_base) {
+  asm volatile("global_load_lds_dword %0, off"
+               :
+               : "v"(gsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_wave_base)));
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

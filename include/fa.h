@@ -75,7 +75,8 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int N, int d, float scale, int causal,
                const uint8_t* block_mask, int dtype, void* stream);
 
-/* Bytes of device workspace fa_backward needs for this shape (0 on bad input). */
+/* Bytes of device workspace fa_backward needs for this shape (0 on bad input):
+ * two fp32 values per (b, h, row), each array padded to 256 bytes. */
 size_t fa_backward_workspace_size(int B, int H, int N, int d);
 
 /*

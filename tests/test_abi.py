@@ -56,8 +56,8 @@ def test_status_strings(lib):
 
 
 def test_workspace_size(lib):
-    assert lib.fa_backward_workspace_size(4, 12, 8192, 64) == 4 * 12 * 8192 * 4
-    assert lib.fa_backward_workspace_size(1, 1, 3, 64) == 256
+    assert lib.fa_backward_workspace_size(4, 12, 8192, 64) == 2 * 4 * 12 * 8192 * 4
+    assert lib.fa_backward_workspace_size(1, 1, 3, 64) == 512
     assert lib.fa_backward_workspace_size(0, 1, 3, 64) == 0
 
 
@@ -97,4 +97,4 @@ def test_backward_validation(lib):
     assert bwd(lib, d=80) == -2
     assert bwd(lib, dtype=0) == -2                      # fp32 backward not built
     assert bwd(lib, ws=None) == -3
-    assert bwd(lib, ws_bytes=2 * 3 * 100 * 4 - 1) == -3
+    assert bwd(lib, ws_bytes=2 * 2 * 3 * 100 * 4 - 1) == -3
