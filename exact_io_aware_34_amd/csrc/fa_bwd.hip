@@ -554,6 +554,522 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   }
 }
 
+// ---- d = 64: unit-pipelined kernels ----
+//
+// Both kernels cut their streamed dimension into 32-row units, two per
+// 64-row tile, and run one block per unit in which the matrix products of
+// the neighbouring units (recomputed S and dP of unit u+1, the gradient
+// products of unit u-1) are issued beside the element-wise work of unit u
+// (P = exp2(S c - lse2), dS = P (dP - D)).  A block has no branch, so one
+// wave keeps the matrix cores and the vector ALUs busy at once.  Masked
+// units (causal diagonal, rows past N, units outside a wave's range) get
+// S = -inf before their element-wise work, so their P and dS are exactly 0.
+
+// dK, dV: one workgroup per (128-key tile, batch*head); wave w owns 32 keys
+// (K, V rows as MFMA operands in VGPRs, dK and dV accumulators) and streams
+// 64-row Q / dO tiles plus their statistics through a 4-slot LDS ring, copies
+// issued two tiles ahead.
+template <typename T, bool CAUSAL, bool SPARSE>
+__global__ __launch_bounds__(256, 2) void bwd_dkdv64_kernel(BwdParams p) {
+  using VT = typename V8<T>::t;
+  constexpr int D = 64, NW = 4, BC = NW * 32, QT = 64, NS = 4;
+  constexpr int DS = D / 16, DB = D / 32, CPR = D / 8;
+  constexpr int TILE = QT * D;                   // elements of one Q (or dO) tile
+  constexpr int DMA_N = QT * CPR / 256;          // 16-byte copies per wave per tile
+  constexpr int OPS = 2 * DMA_N + 1;             // copies per wave per tile (+ statistics)
+  constexpr int STAGE = 2 * TILE;
+  static_assert(BC == MASK_TILE, "a key tile is one block-mask column");
+  static_assert(QT == 64, "statistics: one 64-lane dword copy per quantity");
+  // Slot s: Q tile at [s*STAGE], dO tile at [s*STAGE + TILE] (64 KiB in all,
+  // so every slot offset fits an LDS instruction's immediate), and 4 x 64
+  // floats in st_s[s]: lse2 of the tile's rows, D of its rows (written by
+  // waves 0 and 1; waves 2 and 3 write the same again, so every wave issues
+  // the same copies).
+  __shared__ __attribute__((aligned(1024))) T lds[NS * STAGE];
+  __shared__ __attribute__((aligned(16))) float st_s[NS][NW * 64];
+  __shared__ uint8_t mask_s[SPARSE ? FWD_MAX_MASK_TILES : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, l32 = lane & 31, s16 = lane & 15, gq = lane >> 4;
+  const int N = p.N;
+  const int n_kt = (N + BC - 1) / BC;
+  int bh, j;
+  if (CAUSAL) {
+    // Key tiles with the most query tiles (small j) first across all heads.
+    bh = blockIdx.x % p.BH;
+    j = blockIdx.x / p.BH;
+  } else {
+    const int lid = xcd_remap(blockIdx.x, n_kt * p.BH);
+    bh = lid / n_kt;
+    j = lid - bh * n_kt;
+  }
+  const size_t base = (size_t)bh * N * D;
+  const T* __restrict__ Q = (const T*)p.q + base;
+  const T* __restrict__ K = (const T*)p.k + base;
+  const T* __restrict__ V = (const T*)p.v + base;
+  const T* __restrict__ dO = (const T*)p.dO + base;
+  const float* __restrict__ L2 = p.lse2 + (size_t)bh * N;
+  const float* __restrict__ DEL = p.delta + (size_t)bh * N;
+  const int k0 = j * BC, kw0 = k0 + 32 * wave, my_k = kw0 + l32;
+  const float c = p.scale_log2e;
+
+  if (SPARSE) {
+    for (int i = tid; i < p.mask_tiles; i += 256) mask_s[i] = p.mask[(size_t)i * p.mask_tiles + j];
+    __syncthreads();
+  }
+
+  // Per-lane element offsets in a swizzled tile (rows = queries): A-operand
+  // row reads and B-operand transpose reads; 16-row steps fold into the
+  // immediate offset.
+  int aoff[DS], boff[DB][2];
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds) aoff[ds] = swz_off<D>(l32, 16 * ds + 8 * g);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      boff[db][h] = swz_off<D>(4 * g + (s16 >> 2) + 8 * h, 32 * db + 16 * (gq & 1) + 4 * (s16 & 3));
+  uint32_t doff[DMA_N];
+  int drow[DMA_N];
+#pragma unroll
+  for (int u = 0; u < DMA_N; ++u) {
+    const int pch = (u * NW + wave) * 64 + lane;
+    const int r = pch / CPR, cc = (pch % CPR) ^ swz<D>(r);
+    drow[u] = r;
+    doff[u] = (uint32_t)((r * D + 8 * cc) * (int)sizeof(T));
+  }
+  const uint32_t lds0 = lds_addr(lds);
+
+  const int i_end = (N + QT - 1) / QT;
+  const int i_beg = CAUSAL ? k0 / QT : 0;
+  auto next_active = [&](int i) {
+    if (SPARSE)
+      while (i < i_end && mask_s[(i * QT) / MASK_TILE] == 0) ++i;
+    return i;
+  };
+  // Copy query tile i (Q, dO, statistics) into slot `slot`.  Rows past N read
+  // row N - 1; their scores are masked, so they contribute nothing.
+  auto issue = [&](int i, int slot) {
+    const int qa = i * QT;
+    const uint32_t qd = lds0 + (uint32_t)(slot * STAGE * (int)sizeof(T));
+    const uint32_t od = qd + (uint32_t)(TILE * (int)sizeof(T));
+    const uint32_t sd = lds_addr(&st_s[slot][wave * 64]);
+    if (qa + QT <= N) {
+      const T* qb_ = Q + (size_t)qa * D;
+      const T* ob_ = dO + (size_t)qa * D;
+#pragma unroll
+      for (int u = 0; u < DMA_N; ++u) {
+        const uint32_t wo = (uint32_t)((u * NW + wave) * 64 * 16);
+        dma16_s(qb_, doff[u], qd + wo);
+        dma16_s(ob_, doff[u], od + wo);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < DMA_N; ++u) {
+        const uint32_t wo = (uint32_t)((u * NW + wave) * 64 * 16);
+        const size_t go = (size_t)min(qa + drow[u], N - 1) * D +
+                          (doff[u] / (int)sizeof(T) - drow[u] * D);
+        dma16(Q + go, qd + wo);
+        dma16(dO + go, od + wo);
+      }
+    }
+    const int qs = min(qa + lane, N - 1);
+    dma4((wave & 1) ? DEL + qs : L2 + qs, sd);
+  };
+
+  VT kf[DS], vf[DS];
+  int iq[NS];  // active query tiles n .. n+NS-1 (i_end past the last one)
+  iq[0] = next_active(i_beg);
+#pragma unroll
+  for (int t = 1; t < NS; ++t) iq[t] = iq[t - 1] < i_end ? next_active(iq[t - 1] + 1) : i_end;
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t)
+    if (iq[t] < i_end) issue(iq[t], t);
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds) {
+    kf[ds] = my_k < N ? *(const VT*)(K + (size_t)my_k * D + 16 * ds + 8 * g) : VT{};
+    vf[ds] = my_k < N ? *(const VT*)(V + (size_t)my_k * D + 16 * ds + 8 * g) : VT{};
+  }
+
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+  }
+
+  // S = Q K^T and dP = dO V^T of half h of the tile in slot SL: lane = key,
+  // register r = query 32h + 8(r/4) + 4g + r%4 of the tile.
+  auto sdp = [&](int slot, int h, f32x16& s, f32x16& dp) {
+    const T* qt_ = lds + slot * STAGE + 32 * h * D;
+    s = f32x16{};
+    dp = f32x16{};
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      s = mfma32x32x16(*(const VT*)(qt_ + aoff[ds]), kf[ds], s);
+      dp = mfma32x32x16(*(const VT*)(qt_ + TILE + aoff[ds]), vf[ds], dp);
+    }
+  };
+  // dV += P^T dO and dK += dS^T Q for half h of the tile in slot SL.
+  auto grads = [&](int slot, int h, const VT (&pa)[2], const VT (&dsa)[2]) {
+    const T* qt_ = lds + slot * STAGE + 32 * h * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const VT dof = cat_tr16<VT>(lds_read_tr16(qt_ + TILE + 16 * kk * D + boff[db][0]),
+                                    lds_read_tr16(qt_ + TILE + 16 * kk * D + boff[db][1]));
+        dv[db] = mfma32x32x16(pa[kk], dof, dv[db]);
+        const VT qfr = cat_tr16<VT>(lds_read_tr16(qt_ + 16 * kk * D + boff[db][0]),
+                                    lds_read_tr16(qt_ + 16 * kk * D + boff[db][1]));
+        dk[db] = mfma32x32x16(dsa[kk], qfr, dk[db]);
+      }
+  };
+  // P and dS of half h of the tile in slot SL, rounded to 16-bit operands.
+  auto pds = [&](int slot, int h, const f32x16& s, const f32x16& dp, VT (&pa)[2], VT (&dsa)[2]) {
+    const float* sf = &st_s[slot][32 * h];
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const float4 l4 = *(const float4*)(sf + 8 * rg + 4 * g);
+      const float4 d4 = *(const float4*)(sf + QT + 8 * rg + 4 * g);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+      float pv[4], dsv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pv[e] = fast_exp2(fmaf(s[4 * rg + e], c, -lv[e]));
+        dsv[e] = pv[e] * (dp[4 * rg + e] - dd[e]);
+      }
+      const int kk = rg >> 1, w0 = 2 * (rg & 1);
+      u32x4 pw = __builtin_bit_cast(u32x4, pa[kk]);
+      u32x4 dw = __builtin_bit_cast(u32x4, dsa[kk]);
+      pw[w0] = pack2<T>(pv[0], pv[1]);
+      pw[w0 + 1] = pack2<T>(pv[2], pv[3]);
+      dw[w0] = pack2<T>(dsv[0], dsv[1]);
+      dw[w0 + 1] = pack2<T>(dsv[2], dsv[3]);
+      pa[kk] = __builtin_bit_cast(VT, pw);
+      dsa[kk] = __builtin_bit_cast(VT, dw);
+    }
+  };
+  // Query q sees key my_k iff q >= my_k (causal) and q < N; S = -inf
+  // elsewhere.  Units entirely before this wave's keys are masked whole.
+  auto mask_unit = [&](int qa, f32x16& s) {
+    if ((CAUSAL && qa <= kw0) || qa + 32 > N) {
+      const int first = CAUSAL ? my_k : 0;  // first visible query
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int q = qa + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (q < first || q >= N) s[r] = -INFINITY;
+      }
+    }
+  };
+  // One block: the gradient products of unit u-1 beside the element-wise
+  // work of unit u, then S and dP of unit u+1 (issued last, so the scores of
+  // units u and u+1 are not both live while the vector work runs).
+  auto block = [&](int rslc, int gslc, int eslc, int h, int he, f32x16& s_cur, f32x16& dp_cur,
+                   f32x16& s_nxt, f32x16& dp_nxt, const VT (&pa_p)[2], const VT (&ds_p)[2],
+                   VT (&pa_c)[2], VT (&ds_c)[2]) {
+    grads(gslc, h, pa_p, ds_p);
+    pds(eslc, he, s_cur, dp_cur, pa_c, ds_c);
+    sdp(rslc, h, s_nxt, dp_nxt);
+    sched_interleave<8, 8, 2, 10>();
+    sched_interleave<8, 8, 0, 0>();
+    keep_here(pa_c);
+    keep_here(ds_c);
+  };
+
+  // Units are numbered along the active query tiles, two per tile.  Block u
+  // issues S, dP of unit u+1 and the gradient products of unit u-1 beside the
+  // element-wise work of unit u.  Iteration n runs blocks 2n+1 and 2n+2: it
+  // reads tiles n and n+1, which must have landed; every wave has finished
+  // with tile n-1, whose slot receives tile n+3.
+  f32x16 s_odd, dp_odd, s_even, dp_even;
+  VT pa_odd[2], ds_odd[2], pa_even[2], ds_even[2];
+  if (iq[0] < i_end) {
+    if (iq[2] < i_end) wait_vmcnt<2 * OPS>();
+    else if (iq[1] < i_end) wait_vmcnt<OPS>();
+    else wait_vmcnt<0>();
+    wg_barrier();
+    // Block 0: S, dP of units 0 and 1, P and dS of unit 0.
+    sdp(0, 0, s_even, dp_even);
+    mask_unit(iq[0] * QT, s_even);
+    sdp(0, 1, s_odd, dp_odd);
+    pds(0, 0, s_even, dp_even, pa_even, ds_even);
+  }
+  // One loop body with the slot as a run-time index: four unrolled copies
+  // with constant slots need more registers than the occupancy allows.
+  for (int n = 0; iq[0] < i_end; ++n) {
+    const int SL = n & (NS - 1), SL1 = (n + 1) & (NS - 1);  // slots of tiles n, n+1
+    const int i = iq[0], i1 = iq[1];
+    // Tile n+1 has landed once at most tile n+2's copies are in flight.
+    if (iq[2] < i_end) wait_vmcnt<OPS>();
+    else wait_vmcnt<0>();
+    wg_barrier();
+    if (iq[3] < i_end) issue(iq[3], (SL + 3) & (NS - 1));
+    // Units 2n+1 (second half of tile n) and 2n+2 (first half of tile n+1;
+    // past the last tile it is masked whole and never used).
+    mask_unit(i * QT + 32, s_odd);
+    block(SL1, SL, SL, 0, 1, s_odd, dp_odd, s_even, dp_even, pa_even, ds_even, pa_odd, ds_odd);
+    mask_unit(i1 < i_end ? i1 * QT : N, s_even);
+    block(SL1, SL, SL1, 1, 0, s_even, dp_even, s_odd, dp_odd, pa_odd, ds_odd, pa_even, ds_even);
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t) iq[t] = iq[t + 1];
+    iq[NS - 1] = iq[NS - 2] < i_end ? next_active(iq[NS - 2] + 1) : i_end;
+  }
+
+  // dK = scale * sum dS^T Q, dV = sum P^T dO; lane: column d, register r: key.
+  float* __restrict__ dK = p.dk + base;
+  float* __restrict__ dV = p.dv + base;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kw0 + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (key < N) {
+        dK[(size_t)key * D + 32 * db + l32] = dk[db][r] * p.scale;
+        dV[(size_t)key * D + 32 * db + l32] = dv[db][r];
+      }
+    }
+}
+
+// dQ: one workgroup per (128-query tile, batch*head), query in the lane as in
+// the forward.  64-key K and V tiles stream through two LDS rings (K: 4
+// slots, V: 3), copies issued two tiles ahead.  S^T = K Q^T and
+// dP^T = V dO^T take Q and dO from VGPRs; dQ^T += K^T dS^T reads K
+// transposed.
+template <typename T, bool CAUSAL, bool SPARSE>
+__global__ __launch_bounds__(256, 2) void bwd_dq64_kernel(BwdParams p) {
+  using VT = typename V8<T>::t;
+  constexpr int D = 64, NW = 4, BR = NW * 32, BC = 64, NK = 4, NV = 3;
+  constexpr int DS = D / 16, DB = D / 32, CPR = D / 8;
+  constexpr int TILE = BC * D;                 // elements of one K (or V) tile
+  constexpr int DMA_N = BC * CPR / 256;        // copies per wave per tile
+  static_assert(BR == MASK_TILE, "a query tile is one block-mask row");
+  // K slot s at [s*TILE], V slot s at [(NK+s)*TILE]; rows swizzled.
+  __shared__ __attribute__((aligned(1024))) T kvs[(NK + NV) * TILE];
+  __shared__ uint8_t mask_s[SPARSE ? FWD_MAX_MASK_TILES : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, l32 = lane & 31, s16 = lane & 15, gq = lane >> 4;
+  const int N = p.N;
+  const int n_qt = (N + BR - 1) / BR;
+  int bh, qt;
+  if (CAUSAL) {
+    bh = blockIdx.x % p.BH;
+    qt = n_qt - 1 - blockIdx.x / p.BH;
+  } else {
+    const int lid = xcd_remap(blockIdx.x, n_qt * p.BH);
+    bh = lid / n_qt;
+    qt = lid - bh * n_qt;
+  }
+  const size_t base = (size_t)bh * N * D;
+  const T* __restrict__ Q = (const T*)p.q + base;
+  const T* __restrict__ K = (const T*)p.k + base;
+  const T* __restrict__ V = (const T*)p.v + base;
+  const T* __restrict__ dO = (const T*)p.dO + base;
+  const int q0 = qt * BR + wave * 32;
+  const int my_q = q0 + l32;
+  const float c = p.scale_log2e;
+
+  if (SPARSE) {
+    for (int i = tid; i < p.mask_tiles; i += 256) mask_s[i] = p.mask[(size_t)qt * p.mask_tiles + i];
+    __syncthreads();
+  }
+
+  int koff[DS], toff[DB][2];
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds) koff[ds] = swz_off<D>(l32, 16 * ds + 8 * g);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      toff[db][h] = swz_off<D>(4 * g + (s16 >> 2) + 8 * h, 32 * db + 16 * (gq & 1) + 4 * (s16 & 3));
+  uint32_t doff[DMA_N];
+  int drow[DMA_N];
+#pragma unroll
+  for (int u = 0; u < DMA_N; ++u) {
+    const int pch = (u * NW + wave) * 64 + lane;
+    const int r = pch / CPR, cc = (pch % CPR) ^ swz<D>(r);
+    drow[u] = r;
+    doff[u] = (uint32_t)((r * D + 8 * cc) * (int)sizeof(T));
+  }
+  const uint32_t lds0 = lds_addr(kvs);
+
+  const int n_kt = (N + BC - 1) / BC;
+  int kt_end = n_kt;
+  if (CAUSAL) kt_end = min(kt_end, (min(N, (qt + 1) * BR) + BC - 1) / BC);
+  auto next_active = [&](int jj) {
+    if (SPARSE)
+      while (jj < kt_end && mask_s[(jj * BC) / MASK_TILE] == 0) ++jj;
+    return jj;
+  };
+  // Keys past last_key are invisible to every query of this wave.
+  const int last_key = CAUSAL ? min(N - 1, q0 + 31) : N - 1;
+
+  // Copy tile jj of K (or V) into slot `slot` of its ring.  Rows past N read
+  // row N - 1; their scores are masked, so they contribute nothing.
+  auto issue = [&](const T* src, int jj, uint32_t dst_slot) {
+    const int k0 = jj * BC;
+    const uint32_t dst = lds0 + dst_slot * (uint32_t)(TILE * (int)sizeof(T));
+    if (k0 + BC <= N) {
+      const T* sb = src + (size_t)k0 * D;
+#pragma unroll
+      for (int u = 0; u < DMA_N; ++u)
+        dma16_s(sb, doff[u], dst + (uint32_t)((u * NW + wave) * 64 * 16));
+    } else {
+#pragma unroll
+      for (int u = 0; u < DMA_N; ++u) {
+        const size_t go = (size_t)min(k0 + drow[u], N - 1) * D +
+                          (doff[u] / (int)sizeof(T) - drow[u] * D);
+        dma16(src + go, dst + (uint32_t)((u * NW + wave) * 64 * 16));
+      }
+    }
+  };
+
+  int jq[NK];  // active key tiles n .. n+3 (kt_end past the last one)
+  jq[0] = next_active(0);
+#pragma unroll
+  for (int t = 1; t < NK; ++t) jq[t] = jq[t - 1] < kt_end ? next_active(jq[t - 1] + 1) : kt_end;
+  // Prologue copies K0 V0 K1 V1 K2 V2; iteration n copies K(n+3), V(n+3).
+#pragma unroll
+  for (int t = 0; t < 3; ++t)
+    if (jq[t] < kt_end) {
+      issue(K, jq[t], t);
+      issue(V, jq[t], NK + t);
+    }
+  VT qf[DS], dof[DS];
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds) {
+    qf[ds] = my_q < N ? *(const VT*)(Q + (size_t)my_q * D + 16 * ds + 8 * g) : VT{};
+    dof[ds] = my_q < N ? *(const VT*)(dO + (size_t)my_q * D + 16 * ds + 8 * g) : VT{};
+  }
+  // +inf statistic makes P = 0 on padding rows.
+  const float lq = my_q < N ? p.lse2[(size_t)bh * N + my_q] : INFINITY;
+  const float dq_row = my_q < N ? p.delta[(size_t)bh * N + my_q] : 0.f;
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+
+  // S^T = K Q^T and dP^T = V dO^T of half h of K slot KS / V slot VS: lane =
+  // query, register r = key 32h + 8(r/4) + 4g + r%4 of the tile.
+  auto sdp = [&](int kslot, int vslot, int h, f32x16& s, f32x16& dp) {
+    const T* kt = kvs + kslot * TILE + 32 * h * D;
+    const T* vt = kvs + (NK + vslot) * TILE + 32 * h * D;
+    s = f32x16{};
+    dp = f32x16{};
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      s = mfma32x32x16(*(const VT*)(kt + koff[ds]), qf[ds], s);
+      dp = mfma32x32x16(*(const VT*)(vt + koff[ds]), dof[ds], dp);
+    }
+  };
+  // dQ^T += K^T dS^T for half h of K slot KS (K read transposed).
+  auto dqacc = [&](int kslot, int h, const VT (&dsf)[2]) {
+    const T* kt = kvs + kslot * TILE + 32 * h * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const VT ktf = cat_tr16<VT>(lds_read_tr16(kt + 16 * kk * D + toff[db][0]),
+                                    lds_read_tr16(kt + 16 * kk * D + toff[db][1]));
+        acc[db] = mfma32x32x16(ktf, dsf[kk], acc[db]);
+      }
+  };
+  // dS^T = P^T o (dP^T - D) with P = exp2(S c - lse2), rounded to 16 bits.
+  auto dscores = [&](const f32x16& s, const f32x16& dp, VT (&dsf)[2]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 8 * h + 2 * e;
+        const float p0 = fast_exp2(fmaf(s[r], c, -lq));
+        const float p1 = fast_exp2(fmaf(s[r + 1], c, -lq));
+        w[e] = pack2<T>(p0 * (dp[r] - dq_row), p1 * (dp[r + 1] - dq_row));
+      }
+      dsf[h] = __builtin_bit_cast(VT, w);
+    }
+  };
+  // Keys past this lane's last visible key (causal diagonal, keys >= N)
+  // become -inf; a unit past the wave's range is masked whole.
+  auto mask_unit = [&](int ks, f32x16& s) {
+    if ((CAUSAL && ks + 31 > q0) || ks + 32 > N) {
+      const int lim = min(N - 1, CAUSAL ? my_q : N - 1) - ks - 4 * g;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + (r & 3) > lim) s[r] = -INFINITY;
+    }
+  };
+  auto block = [&](int kslc, int vslc, int gslc, int h, f32x16& s_cur, f32x16& dp_cur,
+                   f32x16& s_nxt, f32x16& dp_nxt, const VT (&ds_p)[2], VT (&ds_c)[2]) {
+    sdp(kslc, vslc, h, s_nxt, dp_nxt);
+    dqacc(gslc, h, ds_p);
+    dscores(s_cur, dp_cur, ds_c);
+    sched_interleave<12, 8, 1, 6>();
+    keep_here(ds_c);
+  };
+
+  // Units are numbered along the active key tiles, two per tile.  Block u
+  // issues S^T, dP^T of unit u+1 and dQ += of unit u-1 beside the
+  // element-wise work of unit u.  Iteration n runs blocks 2n+1 and 2n+2: it
+  // reads K of tiles n and n+1 and V of tile n+1, which must have landed;
+  // every wave has finished with K(n-1) and V(n), whose slots receive K(n+3)
+  // and V(n+3).
+  f32x16 s_odd, dp_odd, s_even, dp_even;
+  VT ds_odd[2], ds_even[2];
+  if (jq[0] < kt_end) {
+    if (jq[2] < kt_end) wait_vmcnt<4 * DMA_N>();
+    else if (jq[1] < kt_end) wait_vmcnt<2 * DMA_N>();
+    else wait_vmcnt<0>();
+    wg_barrier();
+    // Block 0: S^T, dP^T of units 0 and 1, dS of unit 0.
+    sdp(0, 0, 0, s_even, dp_even);
+    mask_unit(jq[0] * BC, s_even);
+    sdp(0, 0, 1, s_odd, dp_odd);
+    dscores(s_even, dp_even, ds_even);
+  }
+  // One loop body with the slots as run-time indices (K: n mod 4, V: n mod 3).
+  int vs0 = 0;  // V slot of tile n
+  for (int n = 0; jq[0] < kt_end; ++n) {
+    const int KS0 = n & (NK - 1), KS1 = (n + 1) & (NK - 1);
+    const int VS1 = vs0 == NV - 1 ? 0 : vs0 + 1;
+    const int jj = jq[0], j1 = jq[1];
+    // K(n+1), V(n+1) have landed once at most tile n+2's copies are in flight.
+    if (jq[2] < kt_end) wait_vmcnt<2 * DMA_N>();
+    else wait_vmcnt<0>();
+    wg_barrier();
+    if (jq[3] < kt_end) {
+      issue(K, jq[3], (n + 3) & (NK - 1));
+      issue(V, jq[3], NK + vs0);  // V(n+3) takes V(n)'s slot
+    }
+    if (jj * BC <= last_key) {
+      mask_unit(jj * BC + 32, s_odd);
+      block(KS1, VS1, KS0, 0, s_odd, dp_odd, s_even, dp_even, ds_even, ds_odd);
+      mask_unit(j1 < kt_end ? j1 * BC : N, s_even);
+      block(KS1, VS1, KS0, 1, s_even, dp_even, s_odd, dp_odd, ds_odd, ds_even);
+    }
+    vs0 = VS1;
+#pragma unroll
+    for (int t = 0; t < NK - 1; ++t) jq[t] = jq[t + 1];
+    jq[NK - 1] = jq[NK - 2] < kt_end ? next_active(jq[NK - 2] + 1) : kt_end;
+  }
+
+  // dQ = scale * dS K; lane: query my_q, register r: column 8*(r/4)+4*g+r%4.
+  if (my_q < N) {
+    float* __restrict__ row = p.dq + base + (size_t)my_q * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg)
+        *(float4*)(row + 32 * db + 8 * rg + 4 * g) =
+            make_float4(acc[db][4 * rg] * p.scale, acc[db][4 * rg + 1] * p.scale,
+                        acc[db][4 * rg + 2] * p.scale, acc[db][4 * rg + 3] * p.scale);
+  }
+}
+
 template <typename T, int D, bool CAUSAL, bool SPARSE>
 hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
   const size_t rows = (size_t)p.BH * p.N;
@@ -562,10 +1078,18 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
       (const T*)p.o, (const T*)p.dO, p.lse, p.delta, p.lse2, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  bwd_dkdv_kernel<T, D, CAUSAL, SPARSE><<<dim3(((p.N + 127) / 128) * p.BH), dim3(256), 0, st>>>(p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  bwd_dq_kernel<T, D, CAUSAL, SPARSE><<<dim3(((p.N + 127) / 128) * p.BH), dim3(256), 0, st>>>(p);
+  const dim3 grid(((p.N + 127) / 128) * p.BH), block(256);
+  if constexpr (D == 64) {
+    bwd_dkdv64_kernel<T, CAUSAL, SPARSE><<<grid, block, 0, st>>>(p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    bwd_dq64_kernel<T, CAUSAL, SPARSE><<<grid, block, 0, st>>>(p);
+  } else {
+    bwd_dkdv_kernel<T, D, CAUSAL, SPARSE><<<grid, block, 0, st>>>(p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    bwd_dq_kernel<T, D, CAUSAL, SPARSE><<<grid, block, 0, st>>>(p);
+  }
   return hipGetLastError();
 }
 

@@ -137,6 +137,32 @@ __device__ __forceinline__ int swz_off(int r, int col) {
   return r * D + 8 * ((col >> 3) ^ swz<D>(r)) + (col & 7);
 }
 
+// Instruction-scheduling hint for the straight-line block emitted just
+// before it: NM matrix-core ops, the first preceded by LEAD LDS reads, each
+// followed by RPM more LDS reads and VPM vector-ALU ops.  It only orders
+// independent instructions (data dependences still hold), so that a wave
+// issues vector work while its own matrix products are in flight.
+template <int NM, int LEAD, int RPM, int VPM>
+__device__ __forceinline__ void sched_interleave() {
+#ifndef FA_NO_SCHED_HINTS
+  if constexpr (LEAD > 0) __builtin_amdgcn_sched_group_barrier(0x100, LEAD, 0);
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (RPM > 0) __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+    if constexpr (VPM > 0) __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+  }
+#endif
+}
+
+// Materialise a pair of 16-bit MFMA operands at this point: an empty
+// volatile asm that reads and writes them, so the arithmetic producing them
+// is not sunk past a later branch (into another scheduling region).
+template <typename VT>
+__device__ __forceinline__ void keep_here(VT (&x)[2]) {
+  asm volatile("" : "+v"(x[0]), "+v"(x[1]));
+}
+
 // True if `pred` holds on any active lane of the wave.
 __device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
 

@@ -41,20 +41,23 @@ template <int V>
 using ic = std::integral_constant<int, V>;
 
 template <typename T, int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(256, FWD16_MIN_WAVES) void fwd16_kernel(FwdParams p) {
+__global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p) {
   using VT = typename V8<T>::t;
   using HT = typename V8<T>::h;
-  constexpr int NW = 4, QBL = fwd16_qblocks(D, SPARSE), QW = 32 * QBL, BR = NW * QW;
-  constexpr int BC = fwd16_kcols(D), KB = BC / 32, KS = BC / 16, NST = FWD16_STAGES;
+  constexpr int NW = 4, BR = 128;              // 4 waves x 32 query rows
+  constexpr int BC = 64;                       // keys per K/V tile (two 32-key units)
+  constexpr int NS = fwd16_slots(D);           // slots per ring
   constexpr int DS = D / 16, DB = D / 32, CPR = D / 8;
   constexpr int TILE = BC * D;                 // elements of one K (or V) tile
-  constexpr int DMA_N = BC * CPR / 256;        // copies per wave per K (or V) tile
-  static_assert(QBL == 1 && BR == MASK_TILE, "one 32-row query block per wave");
-  // Stage st holds K at [2*st*TILE] and V at [(2*st+1)*TILE], rows swizzled.
-  __shared__ __attribute__((aligned(1024))) T kvs[NST * 2 * TILE];
+  constexpr int DMA_N = BC * CPR / 256;        // copies per wave per tile
+  static_assert(BR == MASK_TILE, "a workgroup covers one block-mask row");
+  static_assert(NS == 2 || NS == 3, "ring depth");
+  // K slot s at [s*TILE], V slot s at [(NS+s)*TILE]; rows swizzled.
+  __shared__ __attribute__((aligned(1024))) T kvs[2 * NS * TILE];
   __shared__ uint8_t mask_s[SPARSE ? FWD_MAX_MASK_TILES : 1];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31, s16 = lane & 15, gq = lane >> 4;
   const int N = p.N;
   const int n_qt = (N + BR - 1) / BR;
@@ -74,26 +77,16 @@ __global__ __launch_bounds__(256, FWD16_MIN_WAVES) void fwd16_kernel(FwdParams p
   const T* __restrict__ Q = (const T*)p.q + base;
   const T* __restrict__ K = (const T*)p.k + base;
   const T* __restrict__ V = (const T*)p.v + base;
-  const int q0w = qt * BR + wave * QW;        // first query row of this wave
+  const int q0w = qt * BR + wave * 32;        // first query row of this wave
   const float c = p.scale_log2e;
 
-  // Q^T fragments (B operand): lane holds query q0w + 32*qb + l32.
-  VT qf[QBL][DS];
-#pragma unroll
-  for (int qb = 0; qb < QBL; ++qb) {
-    const int q = q0w + 32 * qb + l32;
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds)
-      qf[qb][ds] = q < N ? *(const VT*)(Q + (size_t)q * D + 16 * ds + 8 * g) : VT{};
-  }
-  if (SPARSE)
+  if (SPARSE) {
     for (int i = tid; i < p.mask_tiles; i += 256) mask_s[i] = p.mask[(size_t)qt * p.mask_tiles + i];
-  // Q and the mask row are in registers/LDS before any copy is in flight.
-  wait_all_loads();
-  __syncthreads();
+    __syncthreads();
+  }
 
   // Per-lane element offsets inside one K or V tile.  The swizzle repeats
-  // every 16 rows, so row offsets that are multiples of 16 (and the stage
+  // every 16 rows, so row offsets that are multiples of 16 (and the slot
   // base, a constant in the unrolled loop below) fold into the instruction's
   // immediate offset.
   int koff[DS], voff[DB][2];
@@ -125,92 +118,86 @@ __global__ __launch_bounds__(256, FWD16_MIN_WAVES) void fwd16_kernel(FwdParams p
       while (jj < kt_end && mask_s[(jj * BC) / MASK_TILE] == 0) ++jj;
     return jj;
   };
-  // Last key tile this wave needs (causal: its rows see keys <= q0w + QW - 1).
-  const int wave_end = CAUSAL ? min(kt_end, (q0w + QW - 1) / BC + 1) : kt_end;
+  // Keys past last_key are invisible to every query of this wave; a unit
+  // starting at ks needs masking iff ks + 31 > plain_key.
+  const int last_key = CAUSAL ? min(N - 1, q0w + 31) : N - 1;
+  const int plain_key = CAUSAL ? min(N - 1, q0w) : N - 1;
 
-  auto issue = [&](int jj, int st) {
+  // Copy tile jj of K (or V) into slot `slot` of its ring.  Rows past N read
+  // row N - 1: those keys are masked out of every score that is used, and
+  // their values meet probability 0.
+  auto issue = [&](const T* src, int jj, int slot, bool is_v) {
     const int k0 = jj * BC;
-    const uint32_t kd = lds0 + (uint32_t)(2 * st * TILE * (int)sizeof(T));
-    const uint32_t vd = kd + (uint32_t)(TILE * (int)sizeof(T));
+    const uint32_t dst = lds0 + (uint32_t)(((is_v ? NS : 0) + slot) * TILE * (int)sizeof(T));
     if (k0 + BC <= N) {
-      const T* kb_ = K + (size_t)k0 * D;
-      const T* vb_ = V + (size_t)k0 * D;
+      const T* sb = src + (size_t)k0 * D;
 #pragma unroll
-      for (int u = 0; u < DMA_N; ++u) {
-        const uint32_t wo = (uint32_t)((u * NW + wave) * 64 * 16);
-        dma16_s(kb_, doff[u], kd + wo);
-        dma16_s(vb_, doff[u], vd + wo);
-      }
+      for (int u = 0; u < DMA_N; ++u)
+        dma16_s(sb, doff[u], dst + (uint32_t)((u * NW + wave) * 64 * 16));
     } else {
-      // Tail tile: rows past N read row N - 1 (zeroed once landed).
 #pragma unroll
       for (int u = 0; u < DMA_N; ++u) {
-        const uint32_t wo = (uint32_t)((u * NW + wave) * 64 * 16);
         const size_t go = (size_t)min(k0 + drow[u], N - 1) * D +
                           (doff[u] / (int)sizeof(T) - drow[u] * D);
-        dma16(K + go, kd + wo);
-        dma16(V + go, vd + wo);
+        dma16(src + go, dst + (uint32_t)((u * NW + wave) * 64 * 16));
       }
     }
   };
-  auto zero_tail = [&](int jj, int st) {
-    const int k0 = jj * BC;
-    if (k0 + BC > N) {
-      for (int pch = tid; pch < BC * CPR; pch += 256)
-        if (k0 + pch / CPR >= N) {
-          *(VT*)(&kvs[2 * st * TILE + 8 * pch]) = VT{};
-          *(VT*)(&kvs[(2 * st + 1) * TILE + 8 * pch]) = VT{};
-        }
-      __syncthreads();
-    }
-  };
 
-  f32x16 o[QBL][DB];
+  // Q^T fragments (B operand): lane holds query q0w + l32.  Loaded after the
+  // first copies are issued; the first use waits for both.
+  int jq[NS + 1];  // active tiles n .. n+NS (kt_end past the last one)
+  jq[0] = next_active(0);
 #pragma unroll
-  for (int qb = 0; qb < QBL; ++qb)
+  for (int i = 1; i <= NS; ++i) jq[i] = jq[i - 1] < kt_end ? next_active(jq[i - 1] + 1) : kt_end;
+  // Prologue copies, in the order K0 V0 K1 [V1 K2]: iteration n then issues
+  // K(n+NS) and V(n+NS-1), each into the slot its predecessor has left.
+  if (jq[0] < kt_end) {
+    issue(K, jq[0], 0, false);
+    issue(V, jq[0], 0, true);
+  }
+  if (jq[1] < kt_end) issue(K, jq[1], 1, false);
+  if (NS == 3) {
+    if (jq[1] < kt_end) issue(V, jq[1], 1, true);
+    if (jq[2] < kt_end) issue(K, jq[2], 2, false);
+  }
+  VT qf[DS];
+  {
+    const int q = q0w + l32;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) o[qb][db] = f32x16{};
-  float m_run[QBL], l_run[QBL];
-#pragma unroll
-  for (int qb = 0; qb < QBL; ++qb) {
-    m_run[qb] = -1e30f;
-    l_run[qb] = 0.f;
+    for (int ds = 0; ds < DS; ++ds)
+      qf[ds] = q < N ? *(const VT*)(Q + (size_t)q * D + 16 * ds + 8 * g) : VT{};
   }
 
-  // S^T[key][query] of one tile (the wave's 32 queries).
-  auto scores1 = [&](auto stc, f32x16 (&sc)[KB]) {
-    const T* kt = kvs + 2 * decltype(stc)::value * TILE;
+  f32x16 o[DB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) sc[kb] = f32x16{};
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  float m_run = -1e30f, l_run = 0.f;
+
+  // ---- work on one 32-key unit ----
+  // S^T[key][query] of half h of the K tile in slot SL.
+  auto s_unit = [&](auto slc, int h, f32x16& s) {
+    const T* kt = kvs + decltype(slc)::value * TILE + 32 * h * D;
+    s = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        const VT kf = *(const VT*)(kt + 32 * kb * D + koff[ds]);
-        sc[kb] = mfma32x32x16(kf, qf[0][ds], sc[kb]);
-      }
+    for (int ds = 0; ds < DS; ++ds) s = mfma32x32x16(*(const VT*)(kt + koff[ds]), qf[ds], s);
   };
-  auto needs_mask = [&](int jj, int qb) {
-    const int k0 = jj * BC;
-    return (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0w + 32 * qb);
-  };
-  // O^T += V^T P^T for the 32 keys of block kb (two 16-key steps).
-  auto pv_half = [&](auto stc, int kb, const VT (&pq)[KS]) {
-    const T* vt = kvs + (2 * decltype(stc)::value + 1) * TILE;
+  // O^T += V^T P^T for half h of the V tile in slot SL (two 16-key steps).
+  auto pv_unit = [&](auto slc, int h, const VT (&pu)[2]) {
+    const T* vt = kvs + (NS + decltype(slc)::value) * TILE + 32 * h * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int kk = 2 * kb + h;
-        const VT vf = cat_tr16<VT>(lds_read_tr16(vt + 16 * kk * D + voff[db][0]),
-                                   lds_read_tr16(vt + 16 * kk * D + voff[db][1]));
-        o[0][db] = mfma32x32x16(vf, pq[kk], o[0][db]);
+      for (int st = 0; st < 2; ++st) {
+        const VT vf = cat_tr16<VT>(lds_read_tr16(vt + 16 * st * D + voff[db][0]),
+                                   lds_read_tr16(vt + 16 * st * D + voff[db][1]));
+        o[db] = mfma32x32x16(vf, pu[st], o[db]);
       }
   };
-  // Exponentials of the 32 keys of block kb against the current reference;
-  // returns the lane's fp32 sum and writes the two 16-bit P^T operands.
-  auto exps_half = [&](const f32x16& sq, VT (&pq)[KS], int kb) {
-    const float mc = m_run[0] * c;
+  // Exponentials of one unit's scores against the current reference; returns
+  // the lane's fp32 sum and writes the two 16-bit P^T operands.
+  auto exps = [&](const f32x16& s, VT (&pu)[2]) {
+    const float mc = m_run * c;
     float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -218,136 +205,138 @@ __global__ __launch_bounds__(256, FWD16_MIN_WAVES) void fwd16_kernel(FwdParams p
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 8 * h + 2 * e;
-        const float e0 = fast_exp2(fmaf(sq[r], c, -mc));
-        const float e1 = fast_exp2(fmaf(sq[r + 1], c, -mc));
+        const float e0 = fast_exp2(fmaf(s[r], c, -mc));
+        const float e1 = fast_exp2(fmaf(s[r + 1], c, -mc));
         ls0 += e0;
         ls1 += e1;
         w[e] = pack2<T>(e0, e1);
       }
-      pq[2 * kb + h] = __builtin_bit_cast(VT, w);
+      pu[h] = __builtin_bit_cast(VT, w);
     }
     return ls0 + ls1;
   };
-  // Softmax and P V of one tile, 32 keys at a time.  Exponentials are taken
-  // against the current reference value first; the reference only moves when
-  // some lane's block sum exceeds 2^8 (so some exponential may exceed 2^8, or
-  // a row had no reference yet): then the block max is taken, O and l are
-  // rescaled by exp(m_old - m_new) (O may already hold the tile's first
-  // block; it is rescaled like every earlier contribution) and the block's
+  // Exponentials are taken against the current reference first; the
+  // reference only moves when some lane's unit sum exceeds 2^8 (so some
+  // exponential may exceed 2^8, or a row had no reference yet): then the unit
+  // max is taken, O and l are rescaled by exp(m_old - m_new) and the unit's
   // exponentials are recomputed.  O, l and lse share the reference, so the
-  // result does not depend on it.
-  auto softmax_pv = [&](auto stc, int jj, f32x16 (&sc)[KB]) {
-    if (needs_mask(jj, 0)) {
-      const int k0 = jj * BC;
-      // Key offset (within the tile) of the last visible key for this lane's
-      // query, less the lane's 4*g row offset in the accumulator.
-      int lim = N - 1 - k0;
-      if (CAUSAL) lim = min(lim, q0w + l32 - k0);
-      lim -= 4 * g;
+  // result does not depend on it.  O already holds every earlier unit
+  // (including the one whose P V was issued in the same block).
+  auto settle = [&](float ls, const f32x16& s, VT (&pu)[2]) {
+    if (wave_any(!(ls <= 256.f))) {
+      float mx = s[0];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      const float m_new = fmaxf(m_run, half_swap_max(mx));
+      const float alpha = fast_exp2((m_run - m_new) * c);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sc[kb][r] = -INFINITY;
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      ls = exps(s, pu);
     }
-    VT pq[KS];
+    l_run += ls;
+  };
+  // Scores of keys past this lane's last visible key (causal diagonal, keys
+  // >= N) become -inf.  A unit past the wave's range is masked entirely, so
+  // its probabilities are exactly 0 and its P V adds nothing.
+  auto mask_unit = [&](int ks, f32x16& s) {
+    if (ks + 31 > plain_key) {
+      const int lim = min(N - 1, CAUSAL ? q0w + l32 : N - 1) - ks - 4 * g;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      float ls = exps_half(sc[kb], pq, kb);
-      if (wave_any(!(ls <= 256.f))) {
-        float mx = sc[kb][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-        const float m_new = fmaxf(m_run[0], half_swap_max(mx));
-        const float alpha = fast_exp2((m_run[0] - m_new) * c);
-        m_run[0] = m_new;
-        l_run[0] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[0][db] *= alpha;
-        ls = exps_half(sc[kb], pq, kb);
-      }
-      l_run[0] += ls;
-      pv_half(stc, kb, pq);
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + (r & 3) > lim) s[r] = -INFINITY;
     }
   };
+  // One block: matrix work of the neighbouring units (scores of the next,
+  // P V of the previous) beside the exponentials of this one, with every LDS
+  // read issued first.
+  auto block = [&](auto kslc, auto vslc, int h, f32x16& s_cur, f32x16& s_nxt,
+                   const VT (&p_prv)[2], VT (&p_cur)[2]) {
+    s_unit(kslc, h, s_nxt);
+    pv_unit(vslc, h, p_prv);
+    const float ls = exps(s_cur, p_cur);
+    if constexpr (D == 64) sched_interleave<8, 12, 0, 7>();
+    else sched_interleave<16, 12, 1, 4>();
+    settle(ls, s_cur, p_cur);
+  };
 
-  // Pipeline over the active tiles t0 < t1 < ...: iteration n issues the
-  // score MFMAs of tile n+1, then the softmax and P V of tile n, so the
-  // exponentials overlap the matrix work still in flight.  Tile n sits in
-  // stage n % NST; tiles n+2 .. n+NST-2 are in flight and tile n+NST-1 is
-  // issued once every wave has left stage (n-1) % NST.
-  int jq[NST];  // tiles n .. n+NST-1 (kt_end past the last one)
-  jq[0] = next_active(0);
-#pragma unroll
-  for (int i = 1; i < NST; ++i) jq[i] = jq[i - 1] < kt_end ? next_active(jq[i - 1] + 1) : kt_end;
-#pragma unroll
-  for (int i = 0; i < NST - 1; ++i)
-    if (jq[i] < kt_end) issue(jq[i], i);
-  // Wait for tile 0, leaving the later prologue tiles in flight.
-  {
-    int inflight = 0;
-#pragma unroll
-    for (int i = 1; i < NST - 1; ++i) inflight += jq[i] < kt_end;
-    if (NST == 4 && inflight == 2) wait_vmcnt<4 * DMA_N>();
-    else if (inflight >= 1) wait_vmcnt<2 * DMA_N>();
-    else wait_vmcnt<0>();
-  }
-  wg_barrier();
-  f32x16 sc[KB];
+  // Units are numbered along the active tiles, two per tile.  Block u
+  // evaluates the softmax of unit u, the scores of unit u+1 and P V of unit
+  // u-1.  Iteration n runs blocks 2n+1 and 2n+2, so it reads only K of tile
+  // n+1 and V of tile n: K(n+1) and V(n) must have landed, and every wave
+  // has finished with K(n) and V(n-1), whose slots then receive K(n+NS) and
+  // V(n+NS-1).  s_odd / p_even carry s(2n+1) and p(2n) between iterations.
+  // Scores computed past the last tile (stale LDS) are never used.
+  f32x16 s_odd, s_even;
+  VT p_odd[2], p_even[2];
+  // Prologue: block 0 (scores of units 0 and 1, softmax of unit 0).
   if (jq[0] < kt_end) {
-    zero_tail(jq[0], 0);
-    if (jq[0] < wave_end) scores1(ic<0>{}, sc);
-  }
-  auto iter = [&](auto stc) {
-    constexpr int ST = decltype(stc)::value;
-    const int j = jq[0], j1 = jq[1];
-    // Tile n+1 must have landed; NST-3 later tiles may stay in flight.
-    if (NST == 4 && jq[2] < kt_end) wait_vmcnt<2 * DMA_N>();
-    else wait_vmcnt<0>();
-    // Tile n+1 is in LDS; every wave has finished with stage (ST - 1) % NST.
+    // Wait for K0, leaving the later prologue copies in flight.
+    if (NS == 3) {
+      if (jq[2] < kt_end) wait_vmcnt<4 * DMA_N>();
+      else if (jq[1] < kt_end) wait_vmcnt<3 * DMA_N>();
+      else wait_vmcnt<DMA_N>();
+    } else {
+      if (jq[1] < kt_end) wait_vmcnt<2 * DMA_N>();
+      else wait_vmcnt<DMA_N>();
+    }
     wg_barrier();
-    if (jq[NST - 1] < kt_end) issue(jq[NST - 1], (ST + NST - 1) % NST);
-    if (j1 < kt_end) zero_tail(j1, (ST + 1) % NST);
-    f32x16 sn[KB];
-    if (j1 < wave_end) scores1(ic<(ST + 1) % NST>{}, sn);
-    if (j < wave_end) softmax_pv(ic<ST>{}, j, sc);
+    s_unit(ic<0>{}, 0, s_even);
+    mask_unit(jq[0] * BC, s_even);
+    s_unit(ic<0>{}, 1, s_odd);
+    settle(exps(s_even, p_even), s_even, p_even);
+  }
+  auto iter = [&](auto slc) {
+    constexpr int SL = decltype(slc)::value;        // n % NS
+    constexpr int SL1 = (SL + 1) % NS;              // slot of tile n+1
+    const int j = jq[0], j1 = jq[1];
+    // K(n+1) and V(n) have landed once at most the copies issued by the
+    // previous iteration (K(n+2), V(n+1)) are in flight.
+    if (NS == 3 && jq[2] < kt_end) wait_vmcnt<2 * DMA_N>();
+    else if (NS == 3 && j1 < kt_end) wait_vmcnt<DMA_N>();
+    else wait_vmcnt<0>();
+    wg_barrier();
+    if (jq[NS] < kt_end) issue(K, jq[NS], SL, false);
+    if (jq[NS - 1] < kt_end) issue(V, jq[NS - 1], (SL + NS - 1) % NS, true);
+    // Units 2n .. 2n+2 start at keys j*BC, j*BC + 32 and j1*BC (j1 = kt_end
+    // past the last tile, which masks unit 2n+2 entirely).
+    if (j * BC <= last_key) {
+      mask_unit(j * BC + 32, s_odd);
+      block(ic<SL1>{}, ic<SL>{}, 0, s_odd, s_even, p_even, p_odd);
+      mask_unit(j1 * BC, s_even);
+      block(ic<SL1>{}, ic<SL>{}, 1, s_even, s_odd, p_odd, p_even);
+    }
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) sc[kb] = sn[kb];
-#pragma unroll
-    for (int i = 0; i < NST - 1; ++i) jq[i] = jq[i + 1];
-    jq[NST - 1] = jq[NST - 2] < kt_end ? next_active(jq[NST - 2] + 1) : kt_end;
+    for (int i = 0; i < NS; ++i) jq[i] = jq[i + 1];
+    jq[NS] = jq[NS - 1] < kt_end ? next_active(jq[NS - 1] + 1) : kt_end;
   };
   while (jq[0] < kt_end) {
     iter(ic<0>{});
     if (jq[0] >= kt_end) break;
-    iter(ic<1>{});
-    if (jq[0] >= kt_end) break;
-    iter(ic<2>{});
-    if constexpr (NST == 4) {
+    iter(ic<1 % NS>{});
+    if constexpr (NS == 3) {
       if (jq[0] >= kt_end) break;
-      iter(ic<3 % NST>{});
+      iter(ic<2>{});
     }
   }
 
   // Epilogue: O = O / l, lse = scale * m + ln(l).
+  const float lt = half_swap_sum(l_run);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  const int q = q0w + l32;
+  if (q < N) {
+    T* orow = (T*)p.o + base + (size_t)q * D;
 #pragma unroll
-  for (int qb = 0; qb < QBL; ++qb) {
-    const float lt = half_swap_sum(l_run[qb]);
-    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-    const int q = q0w + 32 * qb + l32;
-    if (q < N) {
-      T* orow = (T*)p.o + base + (size_t)q * D;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int rg = 0; rg < 4; ++rg) {
+        HT hv;
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          HT h;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) h[e] = (T)(o[qb][db][4 * rg + e] * inv);
-          *(HT*)(orow + 32 * db + 8 * rg + 4 * g) = h;
-        }
-      if (g == 0) p.lse[(size_t)bh * N + q] = lt > 0.f ? m_run[qb] * p.scale + logf(lt) : -INFINITY;
-    }
+        for (int e = 0; e < 4; ++e) hv[e] = (T)(o[db][4 * rg + e] * inv);
+        *(HT*)(orow + 32 * db + 8 * rg + 4 * g) = hv;
+      }
+    if (g == 0) p.lse[(size_t)bh * N + q] = lt > 0.f ? m_run * p.scale + logf(lt) : -INFINITY;
   }
 }
 
@@ -490,8 +479,7 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(FwdParams p) {
 
 template <typename T, int D>
 hipError_t launch16(const FwdParams& p, bool causal, bool sparse, hipStream_t st) {
-  const int br = 4 * 32 * fwd16_qblocks(D, sparse);
-  dim3 grid(((p.N + br - 1) / br) * p.BH), block(256);
+  dim3 grid(((p.N + 127) / 128) * p.BH), block(256);
   if (causal && sparse) fwd16_kernel<T, D, true, true><<<grid, block, 0, st>>>(p);
   else if (causal) fwd16_kernel<T, D, true, false><<<grid, block, 0, st>>>(p);
   else if (sparse) fwd16_kernel<T, D, false, true><<<grid, block, 0, st>>>(p);

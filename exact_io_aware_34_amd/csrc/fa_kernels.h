@@ -10,21 +10,14 @@ namespace fa {
 enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 constexpr int MASK_TILE = 128;  // block-mask granularity (rows and columns)
 constexpr int FWD_BR = 128;     // query rows per fp32 forward workgroup (== MASK_TILE)
-// 32-row query blocks per wave in the 16-bit forward (4 waves per workgroup,
-// so a workgroup covers exactly one 128-row block-mask row).  One block keeps
-// the pipelined loop (scores of the next tile, P V of the current one, and
-// the next tile's exponentials all live at once) within the register budget
-// of several waves per SIMD.
-constexpr int fwd16_qblocks(int, bool) { return 1; }
-// Keys per tile in the 16-bit forward: 64 at d = 64, 32 at d = 128 (four LDS
-// stages of K and V then take 64 KiB, two workgroups per CU).
+// Keys per K/V tile of the dQ backward kernel: 64 at d = 64, 32 at d = 128.
 constexpr int fwd16_kcols(int d) { return d == 64 ? 64 : 32; }
-#ifndef FWD16_STAGES
-#define FWD16_STAGES 3  // LDS stages of the forward's K/V ring (3 or 4)
-#endif
-#ifndef FWD16_MIN_WAVES
-#define FWD16_MIN_WAVES 3  // occupancy target of the forward (waves per SIMD)
-#endif
+// 16-bit forward: 64-key K/V tiles held in two LDS rings (K and V) of this
+// many slots each.  d = 64: 3 slots (48 KiB, three workgroups per CU, copies
+// issued two tiles ahead); d = 128: 2 slots (64 KiB, two workgroups per CU).
+constexpr int fwd16_slots(int d) { return d == 64 ? 3 : 2; }
+// Occupancy the 16-bit forward is compiled for (waves per SIMD).
+constexpr int fwd16_waves(int d) { return d == 64 ? 3 : 2; }
 constexpr int FWD_MAX_MASK_TILES = 2048;  // block-mask columns the forward caches (N <= 262144)
 
 struct FwdParams {
