@@ -773,8 +773,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv64_kernel(BwdParams p) {
     grads(gslc, h, pa_p, ds_p);
     pds(eslc, he, s_cur, dp_cur, pa_c, ds_c);
     sdp(rslc, h, s_nxt, dp_nxt);
-    sched_interleave<8, 8, 2, 10>();
-    sched_interleave<8, 8, 0, 0>();
     keep_here(pa_c);
     keep_here(ds_c);
   };
