@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=4,
+    ap.add_argument("--cpu-heads", type=int, default=12,
                     help="heads of the workload the oracle is timed on")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB device-to-device copy before the steps "
