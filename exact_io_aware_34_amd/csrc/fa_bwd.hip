@@ -795,9 +795,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv64_kernel(BwdParams p) {
     sdp(0, 1, s_odd, dp_odd);
     pds(0, 0, s_even, dp_even, pa_even, ds_even);
   }
-  // One loop body with the slot as a run-time index: four unrolled copies
-  // with constant slots need more registers than the occupancy allows.
-  for (int n = 0; iq[0] < i_end; ++n) {
+  // One iteration; the slot is a run-time index (four unrolled copies with
+  // constant slots need more registers than the occupancy allows).  MASKED
+  // iterations apply the edge masks; the others are branch-free between
+  // their two blocks.
+  int n = 0;
+  auto iteration = [&](auto masked_c) {
+    constexpr bool MASKED = decltype(masked_c)::value;
     const int SL = n & (NS - 1), SL1 = (n + 1) & (NS - 1);  // slots of tiles n, n+1
     const int i = iq[0], i1 = iq[1];
     // Tile n+1 has landed once at most tile n+2's copies are in flight.
@@ -807,14 +811,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv64_kernel(BwdParams p) {
     if (iq[3] < i_end) issue(iq[3], (SL + 3) & (NS - 1));
     // Units 2n+1 (second half of tile n) and 2n+2 (first half of tile n+1;
     // past the last tile it is masked whole and never used).
-    mask_unit(i * QT + 32, s_odd);
+    if constexpr (MASKED) mask_unit(i * QT + 32, s_odd);
     block(SL1, SL, SL, 0, 1, s_odd, dp_odd, s_even, dp_even, pa_even, ds_even, pa_odd, ds_odd);
-    mask_unit(i1 < i_end ? i1 * QT : N, s_even);
+    if constexpr (MASKED) mask_unit(i1 < i_end ? i1 * QT : N, s_even);
     block(SL1, SL, SL1, 1, 0, s_even, dp_even, s_odd, dp_odd, pa_odd, ds_odd, pa_even, ds_even);
 #pragma unroll
     for (int t = 0; t < NS - 1; ++t) iq[t] = iq[t + 1];
     iq[NS - 1] = iq[NS - 2] < i_end ? next_active(iq[NS - 2] + 1) : i_end;
-  }
+    ++n;
+  };
+  // Iterations needing no mask (units 2n+1, 2n+2 past the causal diagonal
+  // and inside N) form one contiguous run: masked ones come before it
+  // (causal diagonal) and after it (row tail).
+  auto interior = [&]() {
+    return (!CAUSAL || iq[0] * QT + 32 > kw0) && iq[1] < i_end && iq[1] * QT + 32 <= N;
+  };
+  while (iq[0] < i_end && !interior()) iteration(std::true_type{});
+  while (iq[0] < i_end && interior()) iteration(std::false_type{});
+  while (iq[0] < i_end) iteration(std::true_type{});
 
   // dK = scale * sum dS^T Q, dV = sum P^T dO; lane: column d, register r: key.
   float* __restrict__ dK = p.dk + base;
@@ -1029,9 +1043,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq64_kernel(BwdParams p) {
     sdp(0, 0, 1, s_odd, dp_odd);
     dscores(s_even, dp_even, ds_even);
   }
-  // One loop body with the slots as run-time indices (K: n mod 4, V: n mod 3).
-  int vs0 = 0;  // V slot of tile n
-  for (int n = 0; jq[0] < kt_end; ++n) {
+  // One iteration; the slots are run-time indices (K: n mod 4, V: n mod 3).
+  // MASKED iterations apply the edge masks; the others are branch-free
+  // between their two blocks.
+  int n = 0, vs0 = 0;  // vs0: V slot of tile n
+  auto iteration = [&](auto masked_c) {
+    constexpr bool MASKED = decltype(masked_c)::value;
     const int KS0 = n & (NK - 1), KS1 = (n + 1) & (NK - 1);
     const int VS1 = vs0 == NV - 1 ? 0 : vs0 + 1;
     const int jj = jq[0], j1 = jq[1];
@@ -1043,17 +1060,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dq64_kernel(BwdParams p) {
       issue(K, jq[3], (n + 3) & (NK - 1));
       issue(V, jq[3], NK + vs0);  // V(n+3) takes V(n)'s slot
     }
-    if (jj * BC <= last_key) {
-      mask_unit(jj * BC + 32, s_odd);
+    if (!MASKED || jj * BC <= last_key) {
+      if constexpr (MASKED) mask_unit(jj * BC + 32, s_odd);
       block(KS1, VS1, KS0, 0, s_odd, dp_odd, s_even, dp_even, ds_even, ds_odd);
-      mask_unit(j1 < kt_end ? j1 * BC : N, s_even);
+      if constexpr (MASKED) mask_unit(j1 < kt_end ? j1 * BC : N, s_even);
       block(KS1, VS1, KS0, 1, s_even, dp_even, s_odd, dp_odd, ds_odd, ds_even);
     }
     vs0 = VS1;
 #pragma unroll
     for (int t = 0; t < NK - 1; ++t) jq[t] = jq[t + 1];
     jq[NK - 1] = jq[NK - 2] < kt_end ? next_active(jq[NK - 2] + 1) : kt_end;
-  }
+    ++n;
+  };
+  // Masked units (causal diagonal, keys >= N) come last in a wave's range,
+  // so the mask-free iterations form a prefix.
+  const int plain_key = CAUSAL ? min(N - 1, q0) : N - 1;
+  while (jq[0] < kt_end && jq[1] < kt_end && jq[1] * BC + 31 <= plain_key) iteration(std::false_type{});
+  while (jq[0] < kt_end) iteration(std::true_type{});
 
   // dQ = scale * dS K; lane: query my_q, register r: column 8*(r/4)+4*g+r%4.
   if (my_q < N) {
