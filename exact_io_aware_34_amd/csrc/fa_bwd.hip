@@ -12,20 +12,19 @@
 //   bwd_pre:  per row, D = rowsum(dO o O) and the log2-domain statistic
 //     lse * log2(e) (+inf for rows with no visible key, so P = 0 there), both
 //     fp32, into the workspace.
-//   bwd_dkdv: one workgroup per (key tile of 128, batch*head).  Wave w owns 32
-//     keys, keeps their K and V rows in VGPRs and dK, dV in fp32
-//     accumulators, and streams the 32-row query tiles that can see them
+//   bwd_dkdv_u: one workgroup per (key tile of 128, batch*head).  Wave w owns
+//     32 keys, keeps their K and V rows as MFMA operands and dK, dV in fp32
+//     accumulators, and streams the 64-row query tiles that can see them
 //     (causal: tiles at or after the key tile; block-sparse: set entries)
-//     through a 3-stage LDS ring filled by direct global->LDS copies (Q and
-//     dO tiles swizzled, plus that tile's statistics).  S = Q K^T and
-//     dP = dO V^T run on v_mfma_f32_32x32x16 with the key in the lane, so
+//     through an LDS ring filled by direct global->LDS copies (Q and dO tiles
+//     swizzled; the tile's statistics in a separate small array).  S = Q K^T
+//     and dP = dO V^T run on v_mfma_f32_32x32x16 with the key in the lane, so
 //     P^T and dS^T for dV += P^T dO and dK += dS^T Q come straight from the
-//     accumulators; dO and Q are read with ds_read_b64_tr_b16.  The S and dP
-//     products of tile n+1 are issued before tile n's element-wise work.
-//   bwd_dq: one workgroup per (query tile of 128, batch*head), the forward's
-//     K/V ring: S^T = K Q^T and dP^T = V dO^T with the query in the lane (so
-//     the statistic and D are per-lane scalars), dS^T in registers, and
-//     dQ^T += K^T dS^T with K read transposed; dQ is stored once.
+//     accumulators; dO and Q are read again with ds_read_b64_tr_b16.
+//   bwd_dq_u: one workgroup per (query tile of 128, batch*head), the
+//     forward's layout: S^T = K Q^T and dP^T = V dO^T with the query in the
+//     lane (so the statistic and D are per-lane scalars), dS^T in registers,
+//     and dQ^T += K^T dS^T with K read transposed; dQ is stored once.
 // Recomputing S, P, dP in both kernels costs two extra products per score,
 // instead of the global atomic adds a single-pass dQ would need (those
 // execute at memory on this part and moved more bytes than the pass computes).
@@ -69,492 +68,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, c
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
-  using VT = typename V8<T>::t;
-  constexpr int NW = 4, BC = NW * 32, QB = 32, NST = 3;
-  constexpr int DS = D / 16, DB = D / 32, CPR = D / 8;
-  constexpr int TILE = QB * D;                   // elements of one Q (or dO) tile
-  constexpr int DMA_N = QB * CPR / 256;          // 16-byte copies per wave per tile
-  constexpr int OPS = 2 * DMA_N + 1;             // copies per wave per tile (+ statistics)
-  constexpr int STATS = NW * 64;                 // floats: each wave's lse2[32], D[32]
-  constexpr int STAGE = 2 * TILE + STATS * 4 / (int)sizeof(T);  // elements per stage
-  static_assert(BC == MASK_TILE, "a key tile is one block-mask column");
-  // Stage st: Q tile at [st*STAGE], dO tile at [st*STAGE + TILE], statistics
-  // after them (wave w: lse2 at float 64*w, D at float 64*w + 32).
-  __shared__ __attribute__((aligned(1024))) T lds[NST * STAGE];
-  __shared__ uint8_t mask_s[SPARSE ? FWD_MAX_MASK_TILES : 1];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 5, l32 = lane & 31, s16 = lane & 15, gq = lane >> 4;
-  const int N = p.N;
-  const int n_kt = (N + BC - 1) / BC;
-  int bh, j;
-  if (CAUSAL) {
-    // Key tiles with the most query tiles (small j) first across all heads.
-    bh = blockIdx.x % p.BH;
-    j = blockIdx.x / p.BH;
-  } else {
-    const int lid = xcd_remap(blockIdx.x, n_kt * p.BH);
-    bh = lid / n_kt;
-    j = lid - bh * n_kt;
-  }
-  const size_t base = (size_t)bh * N * D;
-  const T* __restrict__ Q = (const T*)p.q + base;
-  const T* __restrict__ K = (const T*)p.k + base;
-  const T* __restrict__ V = (const T*)p.v + base;
-  const T* __restrict__ dO = (const T*)p.dO + base;
-  const float* __restrict__ L2 = p.lse2 + (size_t)bh * N;
-  const float* __restrict__ DEL = p.delta + (size_t)bh * N;
-  const int k0 = j * BC, kw0 = k0 + 32 * wave, my_k = kw0 + l32;
-  const float c = p.scale_log2e;
-
-  VT kf[DS], vf[DS];
-#pragma unroll
-  for (int ds = 0; ds < DS; ++ds) {
-    kf[ds] = my_k < N ? *(const VT*)(K + (size_t)my_k * D + 16 * ds + 8 * g) : VT{};
-    vf[ds] = my_k < N ? *(const VT*)(V + (size_t)my_k * D + 16 * ds + 8 * g) : VT{};
-  }
-  if (SPARSE)
-    for (int i = tid; i < p.mask_tiles; i += 256) mask_s[i] = p.mask[(size_t)i * p.mask_tiles + j];
-  wait_all_loads();
-  __syncthreads();
-
-  // Per-lane element offsets in a swizzled tile (rows = queries): A-operand
-  // row reads and B-operand transpose reads; 16-row steps fold into the
-  // immediate offset.
-  int aoff[DS], boff[DB][2];
-#pragma unroll
-  for (int ds = 0; ds < DS; ++ds) aoff[ds] = swz_off<D>(l32, 16 * ds + 8 * g);
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      boff[db][h] = swz_off<D>(4 * g + (s16 >> 2) + 8 * h, 32 * db + 16 * (gq & 1) + 4 * (s16 & 3));
-  uint32_t doff[DMA_N];
-  int drow[DMA_N];
-#pragma unroll
-  for (int u = 0; u < DMA_N; ++u) {
-    const int pch = (u * NW + wave) * 64 + lane;
-    const int r = pch / CPR, cc = (pch % CPR) ^ swz<D>(r);
-    drow[u] = r;
-    doff[u] = (uint32_t)((r * D + 8 * cc) * (int)sizeof(T));
-  }
-  const uint32_t lds0 = lds_addr(lds);
-
-  const int i_end = (N + QB - 1) / QB;
-  const int i_beg = CAUSAL ? k0 / QB : 0;
-  const int wave_beg = CAUSAL ? kw0 / QB : 0;  // earlier tiles see none of this wave's keys
-  auto next_active = [&](int i) {
-    if (SPARSE)
-      while (i < i_end && mask_s[(i * QB) / MASK_TILE] == 0) ++i;
-    return i;
-  };
-  auto issue = [&](int i, int st) {
-    const int qa = i * QB;
-    const uint32_t qd = lds0 + (uint32_t)(st * STAGE * (int)sizeof(T));
-    const uint32_t od = qd + (uint32_t)(TILE * (int)sizeof(T));
-    const uint32_t sd = qd + (uint32_t)(2 * TILE * (int)sizeof(T)) + (uint32_t)(wave * 64 * 4);
-    if (qa + QB <= N) {
-      const T* qb_ = Q + (size_t)qa * D;
-      const T* ob_ = dO + (size_t)qa * D;
-#pragma unroll
-      for (int u = 0; u < DMA_N; ++u) {
-        const uint32_t wo = (uint32_t)((u * NW + wave) * 64 * 16);
-        dma16_s(qb_, doff[u], qd + wo);
-        dma16_s(ob_, doff[u], od + wo);
-      }
-    } else {
-      // Tail tile: rows past N read row N - 1 (zeroed once landed).
-#pragma unroll
-      for (int u = 0; u < DMA_N; ++u) {
-        const uint32_t wo = (uint32_t)((u * NW + wave) * 64 * 16);
-        const size_t go = (size_t)min(qa + drow[u], N - 1) * D +
-                          (doff[u] / (int)sizeof(T) - drow[u] * D);
-        dma16(Q + go, qd + wo);
-        dma16(dO + go, od + wo);
-      }
-    }
-    const int qs = min(qa + l32, N - 1);
-    dma4(g == 0 ? L2 + qs : DEL + qs, sd);
-  };
-  // Tail tile: zero the Q and dO rows past N and give them P = 0.
-  auto zero_tail = [&](int i, int st) {
-    const int qa = i * QB;
-    if (qa + QB > N) {
-      T* qt_ = lds + st * STAGE;
-      for (int pch = tid; pch < QB * CPR; pch += 256)
-        if (qa + pch / CPR >= N) {
-          *(VT*)(qt_ + 8 * pch) = VT{};
-          *(VT*)(qt_ + TILE + 8 * pch) = VT{};
-        }
-      float* sf = (float*)(qt_ + 2 * TILE);
-      for (int t = tid; t < NW * QB; t += 256)
-        if (qa + t % QB >= N) sf[(t / QB) * 64 + t % QB] = INFINITY;
-      __syncthreads();
-    }
-  };
-
-  f32x16 dk[DB], dv[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    dk[db] = f32x16{};
-    dv[db] = f32x16{};
-  }
-
-  // S = Q K^T and dP = dO V^T for one query tile: lane = key, register r =
-  // query 8*(r/4) + 4*g + r%4 of the tile.
-  auto sdp = [&](auto stc, f32x16& s, f32x16& dp) {
-    const T* qt_ = lds + decltype(stc)::value * STAGE;
-    s = f32x16{};
-    dp = f32x16{};
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      s = mfma32x32x16(*(const VT*)(qt_ + aoff[ds]), kf[ds], s);
-      dp = mfma32x32x16(*(const VT*)(qt_ + TILE + aoff[ds]), vf[ds], dp);
-    }
-  };
-  // P, dS and dV += P^T dO, dK += dS^T Q for one query tile.
-  auto update = [&](auto stc, int i, const f32x16& s, const f32x16& dp) {
-    const T* qt_ = lds + decltype(stc)::value * STAGE;
-    const float* sf = (const float*)(qt_ + 2 * TILE) + wave * 64;
-    const int qa = i * QB;
-    const bool need_mask = CAUSAL && qa < kw0 + 31;
-    // Visible iff query offset (within the tile) >= key offset.
-    const int lim = my_k - qa - 4 * g;
-    VT pa[2] = {VT{}, VT{}}, dsa[2] = {VT{}, VT{}};
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const float4 l4 = *(const float4*)(sf + 8 * rg + 4 * g);
-      const float4 d4 = *(const float4*)(sf + 32 + 8 * rg + 4 * g);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-      const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
-      float pv[4], dsv[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * rg + e;
-        pv[e] = fast_exp2(fmaf(s[r], c, -lv[e]));
-        if (need_mask && 8 * rg + e < lim) pv[e] = 0.f;
-        dsv[e] = pv[e] * (dp[r] - dd[e]);
-      }
-      const int kk = rg >> 1, w0 = 2 * (rg & 1);
-      u32x4 pw = __builtin_bit_cast(u32x4, pa[kk]);
-      u32x4 dw = __builtin_bit_cast(u32x4, dsa[kk]);
-      pw[w0] = pack2<T>(pv[0], pv[1]);
-      pw[w0 + 1] = pack2<T>(pv[2], pv[3]);
-      dw[w0] = pack2<T>(dsv[0], dsv[1]);
-      dw[w0 + 1] = pack2<T>(dsv[2], dsv[3]);
-      pa[kk] = __builtin_bit_cast(VT, pw);
-      dsa[kk] = __builtin_bit_cast(VT, dw);
-    }
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int kk = 0; kk < QB / 16; ++kk) {
-        const VT dof = cat_tr16<VT>(lds_read_tr16(qt_ + TILE + 16 * kk * D + boff[db][0]),
-                                    lds_read_tr16(qt_ + TILE + 16 * kk * D + boff[db][1]));
-        dv[db] = mfma32x32x16(pa[kk], dof, dv[db]);
-        const VT qfr = cat_tr16<VT>(lds_read_tr16(qt_ + 16 * kk * D + boff[db][0]),
-                                    lds_read_tr16(qt_ + 16 * kk * D + boff[db][1]));
-        dk[db] = mfma32x32x16(dsa[kk], qfr, dk[db]);
-      }
-  };
-
-  // Pipeline over the active query tiles: iteration n issues S and dP of
-  // tile n+1, then the element-wise work and dV, dK of tile n.  Tile n sits
-  // in stage n % 3; tile n+2 is copied once every wave has left stage n-1.
-  int iq[NST];
-  iq[0] = next_active(i_beg);
-#pragma unroll
-  for (int t = 1; t < NST; ++t) iq[t] = iq[t - 1] < i_end ? next_active(iq[t - 1] + 1) : i_end;
-  if (iq[0] < i_end) issue(iq[0], 0);
-  if (iq[1] < i_end) issue(iq[1], 1);
-  if (iq[1] < i_end) wait_vmcnt<OPS>();
-  else wait_vmcnt<0>();
-  wg_barrier();
-  f32x16 s, dp;
-  if (iq[0] < i_end) {
-    zero_tail(iq[0], 0);
-    if (iq[0] >= wave_beg) sdp(ic<0>{}, s, dp);
-  }
-  auto iter = [&](auto stc) {
-    constexpr int ST = decltype(stc)::value;
-    const int i = iq[0], i1 = iq[1];
-    wait_vmcnt<0>();
-    // Tile n+1 is in LDS; every wave has finished with stage (ST + 2) % 3.
-    wg_barrier();
-    if (iq[2] < i_end) issue(iq[2], (ST + 2) % NST);
-    if (i1 < i_end) zero_tail(i1, (ST + 1) % NST);
-    f32x16 sn, dpn;
-    if (i1 < i_end && i1 >= wave_beg) sdp(ic<(ST + 1) % NST>{}, sn, dpn);
-    if (i >= wave_beg) update(ic<ST>{}, i, s, dp);
-    s = sn;
-    dp = dpn;
-    iq[0] = iq[1];
-    iq[1] = iq[2];
-    iq[2] = iq[1] < i_end ? next_active(iq[1] + 1) : i_end;
-  };
-  while (iq[0] < i_end) {
-    iter(ic<0>{});
-    if (iq[0] >= i_end) break;
-    iter(ic<1>{});
-    if (iq[0] >= i_end) break;
-    iter(ic<2>{});
-  }
-
-  // dK = scale * sum dS^T Q, dV = sum P^T dO; lane: column d, register r: key.
-  float* __restrict__ dK = p.dk + base;
-  float* __restrict__ dV = p.dv + base;
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kw0 + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (key < N) {
-        dK[(size_t)key * D + 32 * db + l32] = dk[db][r] * p.scale;
-        dV[(size_t)key * D + 32 * db + l32] = dv[db][r];
-      }
-    }
-}
-
-template <typename T, int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
-  using VT = typename V8<T>::t;
-  constexpr int NW = 4, BR = NW * 32, NST = 3;
-  constexpr int BC = fwd16_kcols(D), KB = BC / 32, KS = BC / 16;
-  constexpr int DS = D / 16, DB = D / 32, CPR = D / 8;
-  constexpr int TILE = BC * D;                 // elements of one K (or V) tile
-  constexpr int DMA_N = BC * CPR / 256;        // copies per wave per K (or V) tile
-  static_assert(BR == MASK_TILE, "a query tile is one block-mask row");
-  // Stage st holds K at [2*st*TILE] and V at [(2*st+1)*TILE], rows swizzled.
-  __shared__ __attribute__((aligned(1024))) T kvs[NST * 2 * TILE];
-  __shared__ uint8_t mask_s[SPARSE ? FWD_MAX_MASK_TILES : 1];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 5, l32 = lane & 31, s16 = lane & 15, gq = lane >> 4;
-  const int N = p.N;
-  const int n_qt = (N + BR - 1) / BR;
-  int bh, qt;
-  if (CAUSAL) {
-    bh = blockIdx.x % p.BH;
-    qt = n_qt - 1 - blockIdx.x / p.BH;
-  } else {
-    const int lid = xcd_remap(blockIdx.x, n_qt * p.BH);
-    bh = lid / n_qt;
-    qt = lid - bh * n_qt;
-  }
-  const size_t base = (size_t)bh * N * D;
-  const T* __restrict__ Q = (const T*)p.q + base;
-  const T* __restrict__ K = (const T*)p.k + base;
-  const T* __restrict__ V = (const T*)p.v + base;
-  const T* __restrict__ dO = (const T*)p.dO + base;
-  const int q0 = qt * BR + wave * 32;
-  const int my_q = q0 + l32;
-  const float c = p.scale_log2e;
-
-  VT qf[DS], dof[DS];
-#pragma unroll
-  for (int ds = 0; ds < DS; ++ds) {
-    qf[ds] = my_q < N ? *(const VT*)(Q + (size_t)my_q * D + 16 * ds + 8 * g) : VT{};
-    dof[ds] = my_q < N ? *(const VT*)(dO + (size_t)my_q * D + 16 * ds + 8 * g) : VT{};
-  }
-  // +inf statistic makes P = 0 on padding rows.
-  const float lq = my_q < N ? p.lse2[(size_t)bh * N + my_q] : INFINITY;
-  const float dq_row = my_q < N ? p.delta[(size_t)bh * N + my_q] : 0.f;
-  if (SPARSE)
-    for (int i = tid; i < p.mask_tiles; i += 256) mask_s[i] = p.mask[(size_t)qt * p.mask_tiles + i];
-  wait_all_loads();
-  __syncthreads();
-
-  int koff[DS], toff[DB][2];
-#pragma unroll
-  for (int ds = 0; ds < DS; ++ds) koff[ds] = swz_off<D>(l32, 16 * ds + 8 * g);
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      toff[db][h] = swz_off<D>(4 * g + (s16 >> 2) + 8 * h, 32 * db + 16 * (gq & 1) + 4 * (s16 & 3));
-  uint32_t doff[DMA_N];
-  int drow[DMA_N];
-#pragma unroll
-  for (int u = 0; u < DMA_N; ++u) {
-    const int pch = (u * NW + wave) * 64 + lane;
-    const int r = pch / CPR, cc = (pch % CPR) ^ swz<D>(r);
-    drow[u] = r;
-    doff[u] = (uint32_t)((r * D + 8 * cc) * (int)sizeof(T));
-  }
-  const uint32_t lds0 = lds_addr(kvs);
-
-  const int n_kt = (N + BC - 1) / BC;
-  int kt_end = n_kt;
-  if (CAUSAL) kt_end = min(kt_end, (min(N, (qt + 1) * BR) + BC - 1) / BC);
-  auto next_active = [&](int jj) {
-    if (SPARSE)
-      while (jj < kt_end && mask_s[(jj * BC) / MASK_TILE] == 0) ++jj;
-    return jj;
-  };
-  const int wave_end = CAUSAL ? min(kt_end, (q0 + 31) / BC + 1) : kt_end;
-
-  auto issue = [&](int jj, int st) {
-    const int k0 = jj * BC;
-    const uint32_t kd = lds0 + (uint32_t)(2 * st * TILE * (int)sizeof(T));
-    const uint32_t vd = kd + (uint32_t)(TILE * (int)sizeof(T));
-    if (k0 + BC <= N) {
-      const T* kb_ = K + (size_t)k0 * D;
-      const T* vb_ = V + (size_t)k0 * D;
-#pragma unroll
-      for (int u = 0; u < DMA_N; ++u) {
-        const uint32_t wo = (uint32_t)((u * NW + wave) * 64 * 16);
-        dma16_s(kb_, doff[u], kd + wo);
-        dma16_s(vb_, doff[u], vd + wo);
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < DMA_N; ++u) {
-        const uint32_t wo = (uint32_t)((u * NW + wave) * 64 * 16);
-        const size_t go = (size_t)min(k0 + drow[u], N - 1) * D +
-                          (doff[u] / (int)sizeof(T) - drow[u] * D);
-        dma16(K + go, kd + wo);
-        dma16(V + go, vd + wo);
-      }
-    }
-  };
-  auto zero_tail = [&](int jj, int st) {
-    const int k0 = jj * BC;
-    if (k0 + BC > N) {
-      for (int pch = tid; pch < BC * CPR; pch += 256)
-        if (k0 + pch / CPR >= N) {
-          *(VT*)(&kvs[2 * st * TILE + 8 * pch]) = VT{};
-          *(VT*)(&kvs[(2 * st + 1) * TILE + 8 * pch]) = VT{};
-        }
-      __syncthreads();
-    }
-  };
-
-  f32x16 acc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-
-  // S^T = K Q^T (or dP^T = V dO^T with which = 1): lane = query.
-  auto rowprod = [&](auto stc, int which, const VT (&bf)[DS], f32x16 (&out)[KB]) {
-    const T* t = kvs + (2 * decltype(stc)::value + which) * TILE;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) out[kb] = f32x16{};
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds)
-        out[kb] = mfma32x32x16(*(const VT*)(t + 32 * kb * D + koff[ds]), bf[ds], out[kb]);
-  };
-  // P = exp(S - lse) in place, with the causal diagonal and key tail masked.
-  auto probs = [&](int jj, f32x16 (&s)[KB]) {
-    const int k0 = jj * BC;
-    const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0);
-    int lim = N - 1 - k0;
-    if (CAUSAL) lim = min(lim, my_q - k0);
-    lim -= 4 * g;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pv = fast_exp2(fmaf(s[kb][r], c, -lq));
-        if (need_mask && 32 * kb + 8 * (r >> 2) + (r & 3) > lim) pv = 0.f;
-        s[kb][r] = pv;
-      }
-  };
-  // dS^T = P^T o (dP^T - D), rounded to the 16-bit dQ operand.
-  auto dscores = [&](const f32x16 (&pm)[KB], const f32x16 (&dp)[KB], VT (&dsf)[KS]) {
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 8 * h + 2 * e;
-          w[e] = pack2<T>(pm[kb][r] * (dp[kb][r] - dq_row), pm[kb][r + 1] * (dp[kb][r + 1] - dq_row));
-        }
-        dsf[2 * kb + h] = __builtin_bit_cast(VT, w);
-      }
-  };
-  // dQ^T += K^T dS^T (K read transposed).
-  auto dqacc = [&](auto stc, const VT (&dsf)[KS]) {
-    const T* kt = kvs + 2 * decltype(stc)::value * TILE;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        const VT ktf = cat_tr16<VT>(lds_read_tr16(kt + 16 * kk * D + toff[db][0]),
-                                    lds_read_tr16(kt + 16 * kk * D + toff[db][1]));
-        acc[db] = mfma32x32x16(ktf, dsf[kk], acc[db]);
-      }
-  };
-
-  // Pipeline: iteration n issues dP of tile n (the exponentials of tile n,
-  // whose scores came from iteration n-1, overlap it), then the scores of
-  // tile n+1 (dS of tile n overlaps them), then dQ += K^T dS of tile n.
-  int jq[NST];
-  jq[0] = next_active(0);
-#pragma unroll
-  for (int t = 1; t < NST; ++t) jq[t] = jq[t - 1] < kt_end ? next_active(jq[t - 1] + 1) : kt_end;
-  if (jq[0] < kt_end) issue(jq[0], 0);
-  if (jq[1] < kt_end) issue(jq[1], 1);
-  if (jq[1] < kt_end) wait_vmcnt<2 * DMA_N>();
-  else wait_vmcnt<0>();
-  wg_barrier();
-  f32x16 s[KB];
-  if (jq[0] < kt_end) {
-    zero_tail(jq[0], 0);
-    if (jq[0] < wave_end) rowprod(ic<0>{}, 0, qf, s);
-  }
-  auto iter = [&](auto stc) {
-    constexpr int ST = decltype(stc)::value;
-    const int jj = jq[0], j1 = jq[1];
-    wait_vmcnt<0>();
-    // Tile n+1 is in LDS; every wave has finished with stage (ST + 2) % 3.
-    wg_barrier();
-    if (jq[2] < kt_end) issue(jq[2], (ST + 2) % NST);
-    if (j1 < kt_end) zero_tail(j1, (ST + 1) % NST);
-    f32x16 sn[KB];
-    if (jj < wave_end) {
-      f32x16 dp[KB];
-      rowprod(ic<ST>{}, 1, dof, dp);
-      probs(jj, s);
-      if (j1 < wave_end) rowprod(ic<(ST + 1) % NST>{}, 0, qf, sn);
-      VT dsf[KS];
-      dscores(s, dp, dsf);
-      dqacc(ic<ST>{}, dsf);
-    } else if (j1 < wave_end) {
-      rowprod(ic<(ST + 1) % NST>{}, 0, qf, sn);
-    }
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) s[kb] = sn[kb];
-    jq[0] = jq[1];
-    jq[1] = jq[2];
-    jq[2] = jq[1] < kt_end ? next_active(jq[1] + 1) : kt_end;
-  };
-  while (jq[0] < kt_end) {
-    iter(ic<0>{});
-    if (jq[0] >= kt_end) break;
-    iter(ic<1>{});
-    if (jq[0] >= kt_end) break;
-    iter(ic<2>{});
-  }
-
-  // dQ = scale * dS K; lane: query my_q, register r: column 8*(r/4)+4*g+r%4.
-  if (my_q < N) {
-    float* __restrict__ row = p.dq + base + (size_t)my_q * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg)
-        *(float4*)(row + 32 * db + 8 * rg + 4 * g) =
-            make_float4(acc[db][4 * rg] * p.scale, acc[db][4 * rg + 1] * p.scale,
-                        acc[db][4 * rg + 2] * p.scale, acc[db][4 * rg + 3] * p.scale);
-  }
-}
-
-// ---- d = 64: unit-pipelined kernels ----
+// ---- unit-pipelined kernels (d = 64: 2 waves per SIMD; d = 128: 1) ----
 //
 // Both kernels cut their streamed dimension into 32-row units, two per
 // 64-row tile, and run one block per unit in which the matrix products of
@@ -569,10 +83,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
 // (K, V rows as MFMA operands in VGPRs, dK and dV accumulators) and streams
 // 64-row Q / dO tiles plus their statistics through a 4-slot LDS ring, copies
 // issued two tiles ahead.
-template <typename T, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv64_kernel(BwdParams p) {
+template <typename T, int D, bool CAUSAL, bool SPARSE>
+__global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdParams p) {
   using VT = typename V8<T>::t;
-  constexpr int D = 64, NW = 4, BC = NW * 32, QT = 64, NS = 4;
+  constexpr int NW = 4, BC = NW * 32, QT = 64, NS = 4;
   constexpr int DS = D / 16, DB = D / 32, CPR = D / 8;
   constexpr int TILE = QT * D;                   // elements of one Q (or dO) tile
   constexpr int DMA_N = QT * CPR / 256;          // 16-byte copies per wave per tile
@@ -850,10 +364,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv64_kernel(BwdParams p) {
 // slots, V: 3), copies issued two tiles ahead.  S^T = K Q^T and
 // dP^T = V dO^T take Q and dO from VGPRs; dQ^T += K^T dS^T reads K
 // transposed.
-template <typename T, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(256, 2) void bwd_dq64_kernel(BwdParams p) {
+template <typename T, int D, bool CAUSAL, bool SPARSE>
+__global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dq_u_kernel(BwdParams p) {
   using VT = typename V8<T>::t;
-  constexpr int D = 64, NW = 4, BR = NW * 32, BC = 64, NK = 4, NV = 3;
+  constexpr int NW = 4, BR = NW * 32, BC = 64, NK = 4, NV = 3;
   constexpr int DS = D / 16, DB = D / 32, CPR = D / 8;
   constexpr int TILE = BC * D;                 // elements of one K (or V) tile
   constexpr int DMA_N = BC * CPR / 256;        // copies per wave per tile
@@ -1020,7 +534,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq64_kernel(BwdParams p) {
     sdp(kslc, vslc, h, s_nxt, dp_nxt);
     dqacc(gslc, h, ds_p);
     dscores(s_cur, dp_cur, ds_c);
-    sched_interleave<12, 8, 1, 6>();
+    if constexpr (D == 64) sched_interleave<12, 8, 1, 6>();
     keep_here(ds_c);
   };
 
@@ -1100,17 +614,10 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid(((p.N + 127) / 128) * p.BH), block(256);
-  if constexpr (D == 64) {
-    bwd_dkdv64_kernel<T, CAUSAL, SPARSE><<<grid, block, 0, st>>>(p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    bwd_dq64_kernel<T, CAUSAL, SPARSE><<<grid, block, 0, st>>>(p);
-  } else {
-    bwd_dkdv_kernel<T, D, CAUSAL, SPARSE><<<grid, block, 0, st>>>(p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    bwd_dq_kernel<T, D, CAUSAL, SPARSE><<<grid, block, 0, st>>>(p);
-  }
+  bwd_dkdv_u_kernel<T, D, CAUSAL, SPARSE><<<grid, block, 0, st>>>(p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  bwd_dq_u_kernel<T, D, CAUSAL, SPARSE><<<grid, block, 0, st>>>(p);
   return hipGetLastError();
 }
 

@@ -10,14 +10,16 @@ namespace fa {
 enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 constexpr int MASK_TILE = 128;  // block-mask granularity (rows and columns)
 constexpr int FWD_BR = 128;     // query rows per fp32 forward workgroup (== MASK_TILE)
-// Keys per K/V tile of the dQ backward kernel: 64 at d = 64, 32 at d = 128.
-constexpr int fwd16_kcols(int d) { return d == 64 ? 64 : 32; }
 // 16-bit forward: 64-key K/V tiles held in two LDS rings (K and V) of this
 // many slots each.  d = 64: 3 slots (48 KiB, three workgroups per CU, copies
 // issued two tiles ahead); d = 128: 2 slots (64 KiB, two workgroups per CU).
 constexpr int fwd16_slots(int d) { return d == 64 ? 3 : 2; }
 // Occupancy the 16-bit forward is compiled for (waves per SIMD).
 constexpr int fwd16_waves(int d) { return d == 64 ? 3 : 2; }
+// Occupancy of the unit-pipelined backward kernels (waves per SIMD): at
+// d = 128 one wave holds K, V rows and fp32 dK, dV accumulators (512
+// registers) and its workgroup takes most of the CU's LDS.
+constexpr int bwd_u_waves(int d) { return d == 64 ? 2 : 1; }
 constexpr int FWD_MAX_MASK_TILES = 2048;  // block-mask columns the forward caches (N <= 262144)
 
 struct FwdParams {
