@@ -22,6 +22,7 @@ import glob
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -85,29 +86,74 @@ def flops(w, mask):
 
 
 def cpu_baseline(w, inputs, n_heads):
-    """Time the fp64 oracle on `n_heads` heads of the same workload (fwd+bwd)."""
-    import numpy as np
+    """Time the fp64 oracle on `n_heads` heads of the same workload.
+
+    The forward and the backward are timed separately; `value` is their
+    combined FLOPs over their combined time (the same ratio as the GPU step).
+    """
     from threadpoolctl import threadpool_info
 
     import oracle
     mask = None if inputs["mask"] is None else inputs["mask"].numpy()
     heads = [(b, h) for b in range(w.B) for h in range(w.H)][:n_heads]
-    t0 = time.perf_counter()
+    t_fwd = t_bwd = 0.0
     for b, h in heads:
         a = [inputs[n][b, h].double().numpy() for n in ("q", "k", "v")]
+        t0 = time.perf_counter()
         oracle.forward_head(*a, w.scale, causal=w.causal, block_mask=mask)
+        t1 = time.perf_counter()
         if w.backward:
             oracle.backward_head(*a, inputs["do"][b, h].double().numpy(), w.scale,
                                  causal=w.causal, block_mask=mask)
-    dt = time.perf_counter() - t0
+        t_fwd += t1 - t0
+        t_bwd += time.perf_counter() - t1
     f_fwd, f_bwd = flops(w, inputs["mask"])
-    per_head = (f_fwd + (f_bwd if w.backward else 0.0)) / (w.B * w.H)
+    per_head_fwd = f_fwd / (w.B * w.H)
+    per_head_bwd = (f_bwd if w.backward else 0.0) / (w.B * w.H)
+    n = len(heads)
     threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
-    return {"value": per_head * len(heads) / dt / 1e12, "unit": "TFLOPS", "cores": threads,
-            "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"{len(heads)} of {w.B * w.H} heads, forward"
-                      f"{' + backward' if w.backward else ''}, numpy float64, "
-                      f"os.cpu_count()={os.cpu_count()}"}
+    out = {"value": (per_head_fwd + per_head_bwd) * n / (t_fwd + t_bwd) / 1e12, "unit": "TFLOPS",
+           "cores": threads, "kind": "oracle", "seconds": round(t_fwd + t_bwd, 3),
+           "fwd_tflops": per_head_fwd * n / t_fwd / 1e12, "fwd_seconds": round(t_fwd, 3),
+           "sample": f"{n} of {w.B * w.H} heads, forward"
+                     f"{' + backward' if w.backward else ''}, numpy float64, "
+                     f"os.cpu_count()={os.cpu_count()}"}
+    if w.backward:
+        out["bwd_tflops"] = per_head_bwd * n / t_bwd / 1e12
+        out["bwd_seconds"] = round(t_bwd, 3)
+    return out
+
+
+def time_passes(fa, w, tensors, mask, steps, warmup):
+    """Per-step forward and backward times (ms, HIP events on the launch stream)."""
+    import torch
+    q, k, v, do, o, lse, ws, grads = tensors
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.forward(q, k, v, causal=w.causal, scale=w.scale, block_mask=mask, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record(stream)
+        if w.backward:
+            fa.backward(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, block_mask=mask,
+                        workspace=ws, grads=grads)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in events] if w.backward else [0.0]
+    return fwd_ms, bwd_ms, wall
 
 
 def main():
@@ -137,39 +183,15 @@ def main():
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     grads = tuple(torch.empty((B, H, N, d), dtype=torch.float32, device=dev) for _ in range(3))
     ws = torch.empty(fa.workspace_size(B, H, N, d), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        fa.forward(q, k, v, causal=w.causal, scale=w.scale, block_mask=mask, out=o, lse=lse)
-        if ev is not None:
-            ev[1].record(stream)
-        if w.backward:
-            fa.backward(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, block_mask=mask,
-                        workspace=ws, grads=grads)
-        if ev is not None:
-            ev[2].record(stream)
-
     if args.calibrate_copy:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    tensors = (q, k, v, do, o, lse, ws, grads)
+    fwd_ms, bwd_ms, wall = time_passes(fa, w, tensors, mask, args.steps, args.warmup)
 
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
-    bwd_ms = [e[1].elapsed_time(e[2]) for e in events] if w.backward else [0.0]
     mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
     f_fwd, f_bwd = flops(w, mask.cpu() if mask is not None else None)
     if not w.backward:
@@ -203,11 +225,24 @@ def main():
                    "block_sparse": w.sparse, "passes": "fwd+bwd" if w.backward else "fwd",
                    "work_fraction": round(work_fraction(w, inputs["mask"]), 5)},
         "fwd_ms": round(mean(fwd_ms), 4), "bwd_ms": round(mean(bwd_ms), 4),
+        "fwd_ms_median_min": [round(statistics.median(fwd_ms), 4), round(min(fwd_ms), 4)],
+        "bwd_ms_median_min": [round(statistics.median(bwd_ms), 4), round(min(bwd_ms), 4)],
         "fwd_tflops": round(fwd_tf, 2), "fwd_frac_peak": round(fwd_tf / peak, 4),
         "bwd_tflops": None if bwd_tf is None else round(bwd_tf, 2),
         "bwd_frac_peak": None if bwd_tf is None else round(bwd_tf / peak, 4),
         "roofline": roofline,
     }
+    if w.sparse:
+        # Skip efficiency: (T_dense / T_sparse) / (1 / kept fraction), the
+        # dense time from the same kernels with no mask.
+        d_fwd, d_bwd, _ = time_passes(fa, w, tensors, None, max(3, args.steps // 2), 2)
+        kept = float(mask.float().mean())
+        out["skip_efficiency"] = {
+            "kept_tile_fraction": round(kept, 5),
+            "fwd": round(mean(d_fwd) / mean(fwd_ms) * kept, 4),
+            "bwd": round(mean(d_bwd) / mean(bwd_ms) * kept, 4) if w.backward else None,
+            "dense_fwd_ms": round(mean(d_fwd), 4),
+            "dense_bwd_ms": round(mean(d_bwd), 4) if w.backward else None}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_heads)
     print(json.dumps(out))
