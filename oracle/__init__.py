@@ -17,7 +17,10 @@ Pages cited in this package (the reader has these pages):
 * "FlashAttention: Fast and Memory-Efficient Exact Attention with
   IO-Awareness", reading guide (xyznot.com, Portuguese) -- sections
   "Problema e motivação", "Método" (incremental softmax equations and the
-  four per-block steps), "Extensão: Block-Sparse FlashAttention".
+  four per-block steps, "Rastreamento Incremental do Softmax"),
+  "Extensão: Block-Sparse FlashAttention".
+* "Почему Flash Attention быстрее" (sloger.press) -- section "Что это
+  изменило на практике" (decoding: a few queries against a long history).
 
 Every function in this package has at least one pin in
 ``tests/test_oracle_*.py`` that checks it against something other than
@@ -34,6 +37,13 @@ from .attention import (  # noqa: F401
     backward,
     backward_head,
     rowsum_do_o,
+)
+from .decode import (  # noqa: F401
+    combine,
+    decode,
+    decode_allowed,
+    decode_head,
+    split_partials,
 )
 from .online import (  # noqa: F401
     merge_stats,
