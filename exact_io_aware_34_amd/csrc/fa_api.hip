@@ -1,6 +1,7 @@
 // Host side of libfa.so: argument validation and kernel dispatch for the C ABI
 // declared in include/fa.h.  Every check runs before anything is enqueued; an
 // unsupported request returns an error and never runs another code path.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -32,6 +33,43 @@ size_t delta_bytes(int B, int H, int N) {
   return (b + 255) / 256 * 256;
 }
 
+// Decode key ranges.  With n_splits = 0 the count fills the chip once: as
+// many (b*h, range) workgroups as the 256 CUs hold at this kernel's
+// occupancy, ranges no shorter than 512 keys.  Ranges are a multiple of 128
+// keys long; the count actually used is ceil(Nk / range length).
+struct DecSplit {
+  int n, len;
+};
+
+DecSplit dec_split(int B, int H, int Nk, int d, int n_splits) {
+  constexpr int kCUs = 256, kMinLen = 512;
+  const long long bh = (long long)B * H;
+  long long want = n_splits;
+  if (want <= 0) {
+    const long long slots = (long long)kCUs * fa::dec_waves(d);
+    want = std::max(1LL, slots / bh);
+    want = std::min(want, (long long)std::max(1, (Nk + kMinLen - 1) / kMinLen));
+  }
+  want = std::min(want, (long long)((Nk + fa::DEC_SPLIT_ALIGN - 1) / fa::DEC_SPLIT_ALIGN));
+  long long len = (Nk + want - 1) / want;
+  len = (len + fa::DEC_SPLIT_ALIGN - 1) / fa::DEC_SPLIT_ALIGN * fa::DEC_SPLIT_ALIGN;
+  return {(int)((Nk + len - 1) / len), (int)len};
+}
+
+size_t pad256(size_t b) { return (b + 255) / 256 * 256; }
+
+int check_decode(int B, int H, int Nq, int Nk, int d, float scale, int dtype, int n_splits) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1 || n_splits < 0) return FA_ERR_INVALID_ARG;
+  if (Nq > Nk) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype == FA_F32 || Nq > fa::DEC_MAX_NQ) return FA_ERR_UNSUPPORTED;
+  const long long bh = (long long)B * H;
+  if ((long long)Nk * d > (1LL << 31) - 1 || bh * Nk > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -43,7 +81,7 @@ const char* fa_status_string(int status) {
     case FA_OK: return "ok";
     case FA_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad size or dtype, scale not finite and > 0)";
     case FA_ERR_UNSUPPORTED: return "unsupported request (head dim must be 64 or 128; size limits; dtype)";
-    case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_backward_workspace_size()";
+    case FA_ERR_WORKSPACE: return "workspace missing or smaller than the size its *_workspace_size() call returns";
     case FA_ERR_HIP: return "HIP runtime error at kernel launch";
     default: return "unknown status";
   }
@@ -116,6 +154,51 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
   p.scale = scale;
   p.scale_log2e = scale * kLog2e;
   const hipError_t e = fa::launch_backward(p, dtype, d, causal != 0, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_decode_splits(int B, int H, int Nq, int Nk, int d, int n_splits) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < Nq || n_splits < 0 || (d != 64 && d != 128)) return 0;
+  return dec_split(B, H, Nk, d, n_splits).n;
+}
+
+size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d, int n_splits) {
+  const int n = fa_decode_splits(B, H, Nq, Nk, d, n_splits);
+  if (n <= 1) return 0;
+  const size_t rows = (size_t)B * H * n * Nq;
+  return pad256(rows * d * sizeof(float)) + pad256(rows * sizeof(float));
+}
+
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int Nq, int Nk, int d, float scale, int causal,
+              int n_splits, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!tensor_ptr_ok(q) || !tensor_ptr_ok(k) || !tensor_ptr_ok(v) || !tensor_ptr_ok(o))
+    return FA_ERR_INVALID_ARG;
+  if (lse == nullptr || !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
+  const int rc = check_decode(B, H, Nq, Nk, d, scale, dtype, n_splits);
+  if (rc != FA_OK) return rc;
+  const DecSplit sp = dec_split(B, H, Nk, d, n_splits);
+  const size_t need = fa_decode_workspace_size(B, H, Nq, Nk, d, n_splits);
+  if (need > 0 && (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < need))
+    return FA_ERR_WORKSPACE;
+  fa::DecParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  if (need > 0) {
+    const size_t rows = (size_t)B * H * sp.n * Nq;
+    p.o_part = (float*)workspace;
+    p.lse_part = (float*)((char*)workspace + pad256(rows * d * sizeof(float)));
+  }
+  p.BH = B * H;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.n_splits = sp.n;
+  p.split_len = sp.len;
+  p.scale_log2e = scale * kLog2e;
+  const hipError_t e = fa::launch_decode(p, dtype, d, causal != 0, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

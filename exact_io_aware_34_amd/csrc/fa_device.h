@@ -113,6 +113,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 // inserts no wait inside the copy-pipelined loop.
 __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0xF70); }
 
+// Wait until this wave's LDS reads (and other LDS/scalar-memory operations)
+// have completed; no LDS access is moved across it by the compiler.  Used
+// before a direct copy overwrites LDS the same wave has just read.
+__device__ __forceinline__ void lds_reads_done() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
+
 // Workgroup barrier without the memory fence of __syncthreads(): LDS
 // accesses are not moved across it by the compiler, and no wait on
 // outstanding global loads is added.

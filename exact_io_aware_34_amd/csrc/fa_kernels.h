@@ -20,6 +20,12 @@ constexpr int fwd16_waves(int d) { return d == 64 ? 3 : 2; }
 // d = 128 one wave holds K, V rows and fp32 dK, dV accumulators (512
 // registers) and its workgroup takes most of the CU's LDS.
 constexpr int bwd_u_waves(int d) { return d == 64 ? 2 : 1; }
+// Decode: waves per SIMD (== workgroups per CU).  Each workgroup holds four
+// waves' two-slot rings of 32-key K and V tiles: 64 KiB at d = 64, 128 KiB at
+// d = 128.
+constexpr int dec_waves(int d) { return d == 64 ? 2 : 1; }
+constexpr int DEC_MAX_NQ = 16;  // queries per head the decode kernel holds (one MFMA column block)
+constexpr int DEC_SPLIT_ALIGN = 128;  // key-range lengths are multiples of 4 waves x 32 keys
 constexpr int FWD_MAX_MASK_TILES = 2048;  // block-mask columns the forward caches (N <= 262144)
 
 struct FwdParams {
@@ -53,7 +59,21 @@ struct BwdParams {
   float scale, scale_log2e;
 };
 
+struct DecParams {
+  const void* q;   // (B*H, Nq, d)
+  const void* k;   // (B*H, Nk, d)
+  const void* v;
+  void* o;         // (B*H, Nq, d), dtype of q
+  float* lse;      // (B*H, Nq)
+  float* o_part;   // workspace, n_splits > 1: (B*H, n_splits, Nq, d) normalised partial outputs
+  float* lse_part; // workspace, n_splits > 1: (B*H, n_splits, Nq) partial logsumexp
+  int BH, Nq, Nk;
+  int n_splits, split_len;  // key range s = [s * split_len, min(Nk, (s + 1) * split_len))
+  float scale_log2e;
+};
+
 hipError_t launch_forward(FwdParams p, int dtype, int d, bool causal, hipStream_t st);
 hipError_t launch_backward(BwdParams p, int dtype, int d, bool causal, hipStream_t st);
+hipError_t launch_decode(DecParams p, int dtype, int d, bool causal, hipStream_t st);
 
 }  // namespace fa

@@ -8,6 +8,7 @@ library has not been built (there is no other code path).
     from exact_io_aware_34_amd import fa
     o, lse = fa.forward(q, k, v, causal=True)
     dq, dk, dv = fa.backward(q, k, v, o, lse, do, causal=True)
+    o, lse = fa.decode(q_new, k_cache, v_cache)        # Nq <= 16 queries, Nk keys
 """
 
 import ctypes
@@ -29,6 +30,13 @@ _lib.fa_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
 _lib.fa_backward.restype = _i
 _lib.fa_backward_workspace_size.argtypes = [_i, _i, _i, _i]
 _lib.fa_backward_workspace_size.restype = ctypes.c_size_t
+_lib.fa_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _i, _vp,
+                           ctypes.c_size_t, _vp]
+_lib.fa_decode.restype = _i
+_lib.fa_decode_splits.argtypes = [_i, _i, _i, _i, _i, _i]
+_lib.fa_decode_splits.restype = _i
+_lib.fa_decode_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i]
+_lib.fa_decode_workspace_size.restype = ctypes.c_size_t
 _lib.fa_status_string.argtypes = [_i]
 _lib.fa_status_string.restype = ctypes.c_char_p
 _lib.fa_abi_version.restype = _i
@@ -139,3 +147,44 @@ def backward(q, k, v, o, lse, do, causal=False, scale=None, block_mask=None,
     if rc != 0:
         raise FAError(rc)
     return dq, dk, dv
+
+
+def decode_splits(B, H, Nq, Nk, d, n_splits=0) -> int:
+    """Number of key ranges fa_decode uses for this shape (0 on bad input)."""
+    return int(_lib.fa_decode_splits(B, H, Nq, Nk, d, n_splits))
+
+
+def decode_workspace_size(B, H, Nq, Nk, d, n_splits=0) -> int:
+    return int(_lib.fa_decode_workspace_size(B, H, Nq, Nk, d, n_splits))
+
+
+def decode(q, k, v, causal=False, scale=None, n_splits=0, out=None, lse=None, workspace=None,
+           stream=None):
+    """Decode attention: q (B, H, Nq, d) are the last Nq positions of the
+    (B, H, Nk, d) cached keys and values.  Returns (o, lse) like forward()."""
+    for t in (q, k, v):
+        if t.dim() != 4 or not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError("q, k, v must be contiguous 4-d GPU tensors of one dtype")
+    B, H, Nq, d = q.shape
+    if tuple(k.shape[:2]) != (B, H) or k.shape[3] != d or k.shape != v.shape:
+        raise ValueError("k and v must be (B, H, Nk, d) matching q")
+    if q.dtype not in DTYPE_CODES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    Nk = k.shape[2]
+    scale = default_scale(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous():
+        raise ValueError("out must be contiguous, shaped and typed like q")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 (B, H, Nq)")
+    ws_bytes = decode_workspace_size(B, H, Nq, Nk, d, n_splits)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = _lib.fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, scale,
+                        int(bool(causal)), int(n_splits), DTYPE_CODES[q.dtype], _ptr(workspace),
+                        nbytes, _stream(stream))
+    if rc != 0:
+        raise FAError(rc)
+    return o, lse

@@ -28,6 +28,21 @@ sparse_b2h16_n16384_d128_bf16  2, 16, 16384, 128           bf16   128x128 block 
 * The block-sparse mask is Bernoulli(0.25) over 128 x 128 tiles with the
   diagonal tiles always kept, one mask for every (b, h).
 * Scale is 1/sqrt(d) rounded to fp32 (0.125 exactly for d = 64).
+
+Decode workloads (few new queries against a long cached history; q is
+(B, H, Nq, d), k and v are (B, H, Nk, d)):
+
+=================================  ====================  =====  ======================
+name                               B, H, Nq, Nk, d       dtype  notes
+=================================  ====================  =====  ======================
+decode_b8h12_q1_k65536_d64_bf16    8, 12, 1, 65536, 64   bf16   1.5 GiB K/V cache
+=================================  ====================  =====  ======================
+
+Decode draws are seeded per head (see ``draw_decode``) so that any head can be
+regenerated alone on the CPU.  The head geometry (12 heads of d = 64, bf16)
+is the headline workload's; one new query per sequence, 8 sequences, and a
+history of 65 536 keys make the cache several times larger than the MI355X's
+256 MB last-level cache, so the timed scan streams from HBM.
 """
 
 from dataclasses import dataclass, field
@@ -132,3 +147,57 @@ def make(name: str):
                                  with_do=w.backward)
     mask = draw_block_mask(w.N, w.mask_frac, w.mask_seed) if w.sparse else None
     return dict(workload=w, q=q, k=k, v=v, do=do, mask=mask, scale=w.scale, causal=w.causal)
+
+
+@dataclass
+class DecodeWorkload:
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: str
+    causal: bool
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return scale_for(self.d)
+
+
+DECODE_WORKLOADS = {
+    w.name: w
+    for w in [
+        DecodeWorkload("decode_b8h12_q1_k65536_d64_bf16", 8, 12, 1, 65536, 64, "bf16", True,
+                       seed=6),
+    ]
+}
+
+
+def draw_decode_head(b, h, H, Nq, Nk, d, dtype="bf16", seed=0):
+    """(q, k, v) of head (b, h): one fp32 randn((Nq + 2 Nk) * d) from a
+    generator seeded with seed * 1000003 + b * H + h, split in that order."""
+    g = torch.Generator().manual_seed(seed * 1000003 + b * H + h)
+    x = torch.randn(((Nq + 2 * Nk) * d,), generator=g, dtype=torch.float32)
+    x = x.to(TORCH_DTYPES[dtype])
+    q = x[: Nq * d].view(Nq, d)
+    k = x[Nq * d: (Nq + Nk) * d].view(Nk, d)
+    v = x[(Nq + Nk) * d:].view(Nk, d)
+    return q, k, v
+
+
+def draw_decode(B, H, Nq, Nk, d, dtype="bf16", seed=0, device="cpu"):
+    """Seeded decode inputs q (B, H, Nq, d), k, v (B, H, Nk, d) on `device`,
+    filled head by head from ``draw_decode_head``."""
+    dt = TORCH_DTYPES[dtype]
+    q = torch.empty((B, H, Nq, d), dtype=dt, device=device)
+    k = torch.empty((B, H, Nk, d), dtype=dt, device=device)
+    v = torch.empty((B, H, Nk, d), dtype=dt, device=device)
+    for b in range(B):
+        for h in range(H):
+            hq, hk, hv = draw_decode_head(b, h, H, Nq, Nk, d, dtype, seed)
+            q[b, h].copy_(hq)
+            k[b, h].copy_(hk)
+            v[b, h].copy_(hv)
+    return q, k, v

@@ -58,7 +58,7 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, B/H/N < 1, bad dtype, scale not finite > 0 */
   FA_ERR_UNSUPPORTED = -2, /* valid request this build does not implement (e.g. d not 64/128) */
-  FA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than fa_backward_workspace_size() */
+  FA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than its *_workspace_size() */
   FA_ERR_HIP = -4          /* the HIP runtime reported an error at launch */
 } fa_status;
 
@@ -95,6 +95,51 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
                 int B, int H, int N, int d, float scale, int causal,
                 const uint8_t* block_mask, int dtype,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode: a few new queries against a long cached history.
+ *
+ * Decoding has one (or a few) new query rows and a long history of keys and
+ * values, and kernels for it parallelise the scan over that history
+ * ("Почему Flash Attention быстрее", sloger.press, section "Что это изменило
+ * на практике").  q (B,H,Nq,d) holds the LAST Nq positions of a sequence
+ * whose keys and values k, v (B,H,Nk,d) are all cached, 1 <= Nq <= Nk:
+ *   o_i = sum_j P_ij v_j,  P_ij = exp(s_ij - lse_i),  s_ij = scale * <q_i, k_j>,
+ *   lse_i = ln sum_j exp(s_ij), over the visible keys j of query i;
+ * without `causal` every query sees every key; with it query i, at position
+ * Nk - Nq + i, sees keys j <= Nk - Nq + i (the causal rule of "Le masquage
+ * causal", marketmaker.cc page, aligned to the end of the sequence; for
+ * Nq = Nk it is fa_forward's rule).  Writes o (B,H,Nq,d; dtype of q) and lse
+ * (B,H,Nq; fp32, natural log).
+ *
+ * The key range [0, Nk) is cut into n ranges of equal length L (a multiple of
+ * 128 keys; the last range is shorter), each scanned by its own workgroups
+ * with the online-softmax recurrence; a second kernel merges the per-range
+ * (o_s, lse_s) with the incremental-softmax merge ("Rastreamento Incremental
+ * do Softmax", xyznot.com reading guide): lse = ln sum_s exp(lse_s),
+ * o = sum_s exp(lse_s - lse) o_s.  `n_splits` asks for a number of ranges
+ * (0 = let the library fill the GPU); fa_decode_splits() returns the number
+ * actually used, which may be smaller (ranges are at least 128 keys).  With
+ * one range nothing is merged and no workspace is needed.
+ *
+ * `workspace`: device buffer of at least fa_decode_workspace_size() bytes
+ * (same B, H, Nq, Nk, d, n_splits), owned by the caller, scratch for the
+ * duration of the call; may be NULL when that size is 0.
+ * Supported: d in {64, 128}; dtype FA_F16, FA_BF16; Nq <= 16; Nk * d and
+ * B * H * Nk below 2^31.  Nq > Nk, Nq < 1, n_splits < 0 -> FA_ERR_INVALID_ARG;
+ * FA_F32 or Nq > 16 -> FA_ERR_UNSUPPORTED; short workspace -> FA_ERR_WORKSPACE.
+ */
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int Nq, int Nk, int d, float scale, int causal,
+              int n_splits, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Number of key ranges fa_decode uses for these arguments (0 on bad input). */
+int fa_decode_splits(int B, int H, int Nq, int Nk, int d, int n_splits);
+
+/* Bytes of device workspace fa_decode needs (0 with one range or bad input):
+ * per range and query one fp32 partial output row and one fp32 logsumexp,
+ * each array padded to 256 bytes. */
+size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d, int n_splits);
 
 /* Static, human-readable text for a status code. */
 const char* fa_status_string(int status);

@@ -27,6 +27,10 @@ def lib():
     L.fa_backward_workspace_size.argtypes = [i, i, i, i]
     L.fa_backward_workspace_size.restype = ctypes.c_size_t
     L.fa_status_string.restype = ctypes.c_char_p
+    L.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, ctypes.c_size_t, vp]
+    L.fa_decode_splits.argtypes = [i] * 6
+    L.fa_decode_workspace_size.argtypes = [i] * 6
+    L.fa_decode_workspace_size.restype = ctypes.c_size_t
     return L
 
 
@@ -38,8 +42,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "fa_abi_version", "fa_backward", "fa_backward_workspace_size", "fa_forward",
-        "fa_status_string"])
+        "fa_abi_version", "fa_backward", "fa_backward_workspace_size", "fa_decode",
+        "fa_decode_splits", "fa_decode_workspace_size", "fa_forward", "fa_status_string"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -98,3 +102,62 @@ def test_backward_validation(lib):
     assert bwd(lib, dtype=0) == -2                      # fp32 backward not built
     assert bwd(lib, ws=None) == -3
     assert bwd(lib, ws_bytes=2 * 2 * 3 * 100 * 4 - 1) == -3
+
+
+def test_decode_split_choice(lib):
+    S = lib.fa_decode_splits
+
+    def expect(Nk, n):
+        L = -(-Nk // n)
+        L = -(-L // 128) * 128
+        return -(-Nk // L)
+    # Explicit counts: ranges are a multiple of 128 keys long, so fewer may result.
+    for Nk, n in [(1, 1), (1, 8), (1000, 4), (1000, 3), (1000, 7), (129, 2), (65536, 5),
+                  (4097, 33)]:
+        assert S(1, 1, 1, Nk, 64, n) == expect(Nk, n), (Nk, n)
+    assert S(1, 1, 1, 1000, 64, 7) == 4
+    # Automatic: one workgroup per (b*h, range) for every slot of 256 CUs
+    # (2 workgroups per CU at d = 64, 1 at d = 128), ranges of >= 512 keys.
+    assert S(8, 12, 1, 65536, 64, 0) == 5      # 512 // 96
+    assert S(8, 12, 1, 65536, 128, 0) == 2     # 256 // 96
+    assert S(1, 1, 1, 65536, 64, 0) == 128     # 512 slots, but ranges >= 512 keys
+    assert S(1, 1, 1, 300, 64, 0) == 1
+    assert S(64, 16, 1, 8192, 64, 0) == 1
+    # Bad input
+    assert S(0, 1, 1, 10, 64, 0) == 0
+    assert S(1, 1, 5, 4, 64, 0) == 0
+    assert S(1, 1, 1, 10, 96, 0) == 0
+    assert S(1, 1, 1, 10, 64, -1) == 0
+
+
+def test_decode_workspace_size(lib):
+    W = lib.fa_decode_workspace_size
+    assert W(1, 1, 1, 100, 64, 1) == 0
+    assert W(1, 1, 1, 100, 64, 0) == 0         # one range
+    # 8*12*5 ranges x 1 query: 480 rows of 64 fp32 + 480 fp32, each padded to 256 B
+    assert W(8, 12, 1, 65536, 64, 0) == 480 * 64 * 4 + 2048
+    assert W(2, 3, 4, 1000, 128, 4) == 2 * 3 * 4 * 4 * 128 * 4 + 512
+
+
+def dec(lib, q=FAKE, lse=FAKE, B=1, H=2, Nq=1, Nk=1000, d=64, scale=0.125, dtype=2, n=4,
+        ws=FAKE, ws_bytes=1 << 30):
+    return lib.fa_decode(q, FAKE, FAKE, FAKE, lse, B, H, Nq, Nk, d, scale, 1, n, dtype, ws,
+                         ws_bytes, None)
+
+
+def test_decode_validation(lib):
+    assert dec(lib, q=None) == -1
+    assert dec(lib, q=MISALIGNED) == -1
+    assert dec(lib, lse=None) == -1
+    assert dec(lib, Nq=0) == -1
+    assert dec(lib, Nq=5, Nk=4) == -1           # queries are positions of the sequence
+    assert dec(lib, n=-1) == -1
+    assert dec(lib, dtype=7) == -1
+    assert dec(lib, scale=float("nan")) == -1
+    assert dec(lib, d=80) == -2
+    assert dec(lib, dtype=0) == -2              # fp32 decode not built
+    assert dec(lib, Nq=17, Nk=100) == -2        # more than one MFMA column block of queries
+    assert dec(lib, Nk=1 << 26, d=64) == -2
+    assert dec(lib, ws=None) == -3
+    need = lib.fa_decode_workspace_size(1, 2, 1, 1000, 64, 4)
+    assert need > 0 and dec(lib, ws_bytes=need - 1) == -3
