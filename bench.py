@@ -1,7 +1,7 @@
 """Throughput of exact attention forward + backward on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                [--calibrate-copy]
+                [--calibrate-copy] [--decode-workload NAME | --no-decode]
 
 A step is one forward pass and one backward pass (every kernel of the path:
 forward, backward preprocess, backward main) over the workload's synthetic
@@ -9,6 +9,12 @@ inputs, which are resident in HBM before the timed region starts.  FLOPs are
 counted as 4*N^2*d per head for the forward and 10*N^2*d per head for the
 backward, halved for causal masking and scaled by the fraction of 128x128
 tiles the block mask keeps.  One JSON line is printed.
+
+The decode path (fa_decode: a few queries against a long cached K/V history)
+is timed after the steps on its own workload and reported in the `decode`
+object of the same line: call time, algorithmic HBM bytes per call (16-bit K
+and V read once, q read, o and lse written) over that time against the
+8 TB/s HBM peak, and the oracle's rate on a few heads.
 
 `roofline.traffic` comes from profiles/hbm_traffic_<workload>.json (FETCH_SIZE
 and WRITE_SIZE counter runs of this script, scaled by the same counters on a
@@ -43,6 +49,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=12,
                     help="heads of the workload the oracle is timed on")
+    ap.add_argument("--decode-workload", default="decode_b8h12_q1_k65536_d64_bf16")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-cpu-heads", type=int, default=24)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB device-to-device copy before the steps "
                          "(reference kernel for HBM byte counters)")
@@ -156,6 +165,83 @@ def time_passes(fa, w, tensors, mask, steps, warmup):
     return fwd_ms, bwd_ms, wall
 
 
+def decode_bytes(w):
+    """Algorithmic HBM bytes of one fa_decode call: K and V read once, q read,
+    o written (16-bit), lse written (fp32)."""
+    e = 2
+    return w.B * w.H * (2 * w.Nk * w.d * e + 2 * w.Nq * w.d * e + 4 * w.Nq)
+
+
+def decode_cpu_baseline(w, n_heads):
+    """The oracle's decode on `n_heads` heads, as bytes-equivalent GB/s."""
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from exact_io_aware_34_amd import workloads as W
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)][:n_heads]
+    t = 0.0
+    for b, h in heads:
+        q, k, v = (x.double().numpy() for x in
+                   W.draw_decode_head(b, h, w.H, w.Nq, w.Nk, w.d, w.dtype, seed=w.seed))
+        t0 = time.perf_counter()
+        oracle.decode_head(q, k, v, w.scale, w.causal)
+        t += time.perf_counter() - t0
+    threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+    per_head = decode_bytes(w) / (w.B * w.H)
+    return {"value": round(per_head * len(heads) / t / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "seconds": round(t, 3),
+            "sample": f"{len(heads)} of {w.B * w.H} heads, numpy float64 on the 16-bit "
+                      f"inputs, os.cpu_count()={os.cpu_count()}"}
+
+
+def bench_decode(fa, name, steps, warmup, cpu_heads, with_cpu):
+    import torch
+
+    from exact_io_aware_34_amd import workloads as W
+    w = W.DECODE_WORKLOADS[name]
+    q, k, v = W.draw_decode(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, seed=w.seed, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=q.device)
+    n = fa.decode_splits(w.B, w.H, w.Nq, w.Nk, w.d, 0)
+    ws = torch.empty(max(1, fa.decode_workspace_size(w.B, w.H, w.Nq, w.Nk, w.d, 0)),
+                     dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        fa.decode(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    mean_ms = sum(ms) / len(ms)
+    byts = decode_bytes(w)
+    gbs = byts / (mean_ms * 1e-3) / 1e9
+    rec = recorded_traffic(name)
+    out = {"workload": name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+           "causal": w.causal, "dtype": w.dtype, "key_ranges": n, "workgroups": w.B * w.H * n,
+           "ms": round(mean_ms, 4),
+           "ms_median_min": [round(statistics.median(ms), 4), round(min(ms), 4)],
+           "keys_per_s": round(w.B * w.H * w.Nk / (mean_ms * 1e-3), 1),
+           "roofline": {"bound": "hbm", "kernel": "fa_decode (dec_kernel + dec_combine)",
+                        "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_call": byts,
+                        "traffic": None if rec is None else rec["bytes_per_call"].get("decode"),
+                        "avg_ms": round(mean_ms, 4)}}
+    if with_cpu:
+        out["cpu_baseline"] = decode_cpu_baseline(w, cpu_heads)
+    del q, k, v, o, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -243,6 +329,9 @@ def main():
             "bwd": round(mean(d_bwd) / mean(bwd_ms) * kept, 4) if w.backward else None,
             "dense_fwd_ms": round(mean(d_fwd), 4),
             "dense_bwd_ms": round(mean(d_bwd), 4) if w.backward else None}
+    if not args.no_decode:
+        out["decode"] = bench_decode(fa, args.decode_workload, args.steps, args.warmup,
+                                     args.decode_cpu_heads, not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_heads)
     print(json.dumps(out))

@@ -33,22 +33,24 @@ size_t delta_bytes(int B, int H, int N) {
   return (b + 255) / 256 * 256;
 }
 
-// Decode key ranges.  With n_splits = 0 the count fills the chip once: as
-// many (b*h, range) workgroups as the 256 CUs hold at this kernel's
-// occupancy, ranges no shorter than 512 keys.  Ranges are a multiple of 128
-// keys long; the count actually used is ceil(Nk / range length).
+// Decode key ranges.  With n_splits = 0 the count aims at about 192
+// (b*h, range) workgroups -- one workgroup on each of three quarters of the
+// 256 CUs -- with ranges no shorter than 512 keys.  Measured on the decode
+// scan: one workgroup per CU streams fastest, and a count that puts two
+// workgroups on some CUs but one on others ends in a tail on the doubly
+// loaded ones.  Ranges are a multiple of 128 keys long; the count actually
+// used is ceil(Nk / range length).
 struct DecSplit {
   int n, len;
 };
 
-DecSplit dec_split(int B, int H, int Nk, int d, int n_splits) {
-  constexpr int kCUs = 256, kMinLen = 512;
+DecSplit dec_split(int B, int H, int Nk, int n_splits) {
+  constexpr long long kTargetWGs = 192, kMinLen = 512;
   const long long bh = (long long)B * H;
   long long want = n_splits;
   if (want <= 0) {
-    const long long slots = (long long)kCUs * fa::dec_waves(d);
-    want = std::max(1LL, slots / bh);
-    want = std::min(want, (long long)std::max(1, (Nk + kMinLen - 1) / kMinLen));
+    want = std::max(1LL, (kTargetWGs + bh / 2) / bh);
+    want = std::min(want, std::max(1LL, (Nk + kMinLen - 1) / kMinLen));
   }
   want = std::min(want, (long long)((Nk + fa::DEC_SPLIT_ALIGN - 1) / fa::DEC_SPLIT_ALIGN));
   long long len = (Nk + want - 1) / want;
@@ -159,7 +161,7 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
 
 int fa_decode_splits(int B, int H, int Nq, int Nk, int d, int n_splits) {
   if (B < 1 || H < 1 || Nq < 1 || Nk < Nq || n_splits < 0 || (d != 64 && d != 128)) return 0;
-  return dec_split(B, H, Nk, d, n_splits).n;
+  return dec_split(B, H, Nk, n_splits).n;
 }
 
 size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d, int n_splits) {
@@ -177,7 +179,7 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
   if (lse == nullptr || !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
   const int rc = check_decode(B, H, Nq, Nk, d, scale, dtype, n_splits);
   if (rc != FA_OK) return rc;
-  const DecSplit sp = dec_split(B, H, Nk, d, n_splits);
+  const DecSplit sp = dec_split(B, H, Nk, n_splits);
   const size_t need = fa_decode_workspace_size(B, H, Nq, Nk, d, n_splits);
   if (need > 0 && (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < need))
     return FA_ERR_WORKSPACE;

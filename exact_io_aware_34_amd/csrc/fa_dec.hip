@@ -23,7 +23,8 @@
 //     their own online-softmax state; the four states merge once at the end.
 //   * Each wave owns a two-slot LDS ring; a step's K and V rows (32 x d each)
 //     arrive by direct global->LDS copies issued one step ahead, so only the
-//     wave's own vmcnt is waited on.
+//     wave's own vmcnt is waited on.  The copies use the non-temporal cache
+//     policy: every K/V byte is read once per call.
 //   * Scores are S^T = K Q^T on v_mfma_f32_16x16x32 with the queries padded to
 //     16 columns (Q^T stays in VGPRs): lane l holds query l % 16 at 8 of the
 //     32 keys, which are exactly the 8 contraction slots it supplies to
@@ -117,18 +118,18 @@ __global__ __launch_bounds__(256, dec_waves(D)) void dec_kernel(DecParams p) {
       const T* vb = V + (size_t)k0 * D;
 #pragma unroll
       for (int u = 0; u < DMA_N; ++u)
-        dma16_s(kb, (uint32_t)((drow[u] * D + kcol[u]) * (int)sizeof(T)), kdst + 1024u * u);
+        dma16_s_stream(kb, (uint32_t)((drow[u] * D + kcol[u]) * (int)sizeof(T)), kdst + 1024u * u);
 #pragma unroll
       for (int u = 0; u < DMA_N; ++u)
-        dma16_s(vb, (uint32_t)((drow[u] * D + vcol[u]) * (int)sizeof(T)), vdst + 1024u * u);
+        dma16_s_stream(vb, (uint32_t)((drow[u] * D + vcol[u]) * (int)sizeof(T)), vdst + 1024u * u);
     } else {
       // Rows past Nk read row Nk - 1: their scores are masked to -inf and
       // their values meet probability 0.
 #pragma unroll
       for (int u = 0; u < DMA_N; ++u) {
         const size_t row = (size_t)min(k0 + drow[u], Nk - 1) * D;
-        dma16(K + row + kcol[u], kdst + 1024u * u);
-        dma16(V + row + vcol[u], vdst + 1024u * u);
+        dma16_stream(K + row + kcol[u], kdst + 1024u * u);
+        dma16_stream(V + row + vcol[u], vdst + 1024u * u);
       }
     }
   };

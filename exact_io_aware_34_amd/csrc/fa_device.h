@@ -94,6 +94,22 @@ __device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32
                : "v"(voff), "s"(sbase), "{m0}"(__builtin_amdgcn_readfirstlane(lds_wave_base)));
 }
 
+// Streaming variants: the same copies with the non-temporal cache policy, for
+// data each call reads exactly once (a decode scan over the key/value
+// history).  Keeping such lines out of the way of reused data lets a
+// streaming read run closer to the HBM rate than the default policy does.
+__device__ __forceinline__ void dma16_stream(const void* gsrc, uint32_t lds_wave_base) {
+  asm volatile("global_load_lds_dwordx4 %0, off nt"
+               :
+               : "v"(gsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_wave_base)));
+}
+__device__ __forceinline__ void dma16_s_stream(const void* sbase, uint32_t voff,
+                                               uint32_t lds_wave_base) {
+  asm volatile("global_load_lds_dwordx4 %0, %1 nt"
+               :
+               : "v"(voff), "s"(sbase), "{m0}"(__builtin_amdgcn_readfirstlane(lds_wave_base)));
+}
+
 // 4-byte-per-lane variant: lane l's dword lands at lds_wave_base + 4 * l.
 __device__ __forceinline__ void dma4(const void* gsrc, uint32_t lds_wave_base) {
   asm volatile("global_load_lds_dword %0, off"

@@ -116,11 +116,14 @@ def test_decode_split_choice(lib):
                   (4097, 33)]:
         assert S(1, 1, 1, Nk, 64, n) == expect(Nk, n), (Nk, n)
     assert S(1, 1, 1, 1000, 64, 7) == 4
-    # Automatic: one workgroup per (b*h, range) for every slot of 256 CUs
-    # (2 workgroups per CU at d = 64, 1 at d = 128), ranges of >= 512 keys.
-    assert S(8, 12, 1, 65536, 64, 0) == 5      # 512 // 96
-    assert S(8, 12, 1, 65536, 128, 0) == 2     # 256 // 96
-    assert S(1, 1, 1, 65536, 64, 0) == 128     # 512 slots, but ranges >= 512 keys
+    # Automatic: about 192 (b*h, range) workgroups, ranges of >= 512 keys.
+    assert S(8, 12, 1, 65536, 64, 0) == 2      # 96 heads x 2
+    assert S(8, 12, 1, 65536, 128, 0) == 2
+    assert S(4, 12, 1, 65536, 64, 0) == 4
+    assert S(1, 12, 1, 262144, 64, 0) == 16
+    assert S(1, 8, 1, 131072, 128, 0) == 24
+    assert S(2, 40, 1, 65536, 64, 0) == 2      # 192 / 80 rounds to 2
+    assert S(1, 1, 1, 65536, 64, 0) == 128     # 192 wanted, but ranges >= 512 keys
     assert S(1, 1, 1, 300, 64, 0) == 1
     assert S(64, 16, 1, 8192, 64, 0) == 1
     # Bad input
@@ -134,8 +137,8 @@ def test_decode_workspace_size(lib):
     W = lib.fa_decode_workspace_size
     assert W(1, 1, 1, 100, 64, 1) == 0
     assert W(1, 1, 1, 100, 64, 0) == 0         # one range
-    # 8*12*5 ranges x 1 query: 480 rows of 64 fp32 + 480 fp32, each padded to 256 B
-    assert W(8, 12, 1, 65536, 64, 0) == 480 * 64 * 4 + 2048
+    # 8*12*2 ranges x 1 query: 192 rows of 64 fp32 + 192 fp32, each padded to 256 B
+    assert W(8, 12, 1, 65536, 64, 0) == 192 * 64 * 4 + 768
     assert W(2, 3, 4, 1000, 128, 4) == 2 * 3 * 4 * 4 * 128 * 4 + 512
 
 

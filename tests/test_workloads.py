@@ -63,3 +63,24 @@ def test_named_workloads_shapes():
     assert (w.B, w.H, w.N, w.d, w.dtype, w.causal) == (4, 12, 8192, 64, "bf16", True)
     small = W.make("dense_n256_d64_f32")
     assert small["q"].shape == (1, 1, 256, 64) and small["do"] is None
+
+
+def test_decode_draws_are_per_head():
+    q, k, v = W.draw_decode(2, 3, 4, 50, 8, "f16", seed=9)
+    assert q.shape == (2, 3, 4, 8) and k.shape == (2, 3, 50, 8) and v.dtype == torch.float16
+    for b in range(2):
+        for h in range(3):
+            hq, hk, hv = W.draw_decode_head(b, h, 3, 4, 50, 8, "f16", seed=9)
+            assert torch.equal(hq, q[b, h]) and torch.equal(hk, k[b, h]) and torch.equal(hv, v[b, h])
+    # one generator per head, seeded seed * 1000003 + b * H + h, split q | k | v
+    g = torch.Generator().manual_seed(9 * 1000003 + 1 * 3 + 2)
+    raw = torch.randn(((4 + 100) * 8,), generator=g).to(torch.float16)
+    assert torch.equal(raw[32:32 + 400].view(50, 8), k[1, 2])
+    assert not torch.equal(k[0, 0], k[0, 1])
+
+
+def test_decode_workload_streams_from_hbm():
+    w = W.DECODE_WORKLOADS["decode_b8h12_q1_k65536_d64_bf16"]
+    cache_bytes = 2 * w.B * w.H * w.Nk * w.d * 2
+    assert cache_bytes > 4 * 256 * 2 ** 20        # several times the 256 MB last-level cache
+    assert (w.H, w.d, w.dtype) == (W.WORKLOADS[W.HEADLINE].H, W.WORKLOADS[W.HEADLINE].d, "bf16")
