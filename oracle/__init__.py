@@ -21,6 +21,8 @@ Pages cited in this package (the reader has these pages):
   "Extensão: Block-Sparse FlashAttention".
 * "Почему Flash Attention быстрее" (sloger.press) -- section "Что это
   изменило на практике" (decoding: a few queries against a long history).
+* marketmaker.cc page, section "FA3 : Mécanique de la trémie", point 3 (FP8
+  with incoherent processing: random rotation, then per-block quantisation).
 
 Every function in this package has at least one pin in
 ``tests/test_oracle_*.py`` that checks it against something other than
@@ -44,6 +46,15 @@ from .decode import (  # noqa: F401
     decode_allowed,
     decode_head,
     split_partials,
+)
+from .fp8 import (  # noqa: F401
+    E4M3_MAX,
+    block_quantize,
+    e4m3,
+    fp8_forward,
+    fp8_forward_head,
+    hadamard,
+    rotate,
 )
 from .online import (  # noqa: F401
     merge_stats,
