@@ -72,6 +72,56 @@ int check_decode(int B, int H, int Nq, int Nk, int d, float scale, int dtype, in
   return FA_OK;
 }
 
+// FP8 workspace regions, in order, each padded to 256 bytes.
+struct Fp8Layout {
+  size_t q8, k8, v8t, sq, sk, sv, total;
+};
+
+Fp8Layout fp8_layout(int B, int H, int N, int d) {
+  const size_t bh = (size_t)B * H, nt = ((size_t)N + 63) / 64;
+  const size_t op = pad256(bh * nt * 64 * d), sc = pad256(bh * nt * sizeof(float));
+  Fp8Layout l{};
+  l.q8 = 0;
+  l.k8 = op;
+  l.v8t = 2 * op;
+  l.sq = 3 * op;
+  l.sk = 3 * op + sc;
+  l.sv = 3 * op + 2 * sc;
+  l.total = 3 * op + 3 * sc;
+  return l;
+}
+
+int fp8_setup(fa::Fp8Params& p, const void* q, const void* k, const void* v, int B, int H, int N,
+              int d, float scale, int dtype, const int8_t* signs, void* workspace,
+              size_t workspace_bytes) {
+  if (!tensor_ptr_ok(q) || !tensor_ptr_ok(k) || !tensor_ptr_ok(v)) return FA_ERR_INVALID_ARG;
+  const int rc = check_common(B, H, N, d, scale, dtype);
+  if (rc != FA_OK) return rc;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  const Fp8Layout l = fp8_layout(B, H, N, d);
+  if (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < l.total)
+    return FA_ERR_WORKSPACE;
+  char* w = (char*)workspace;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.signs = signs;
+  p.q8 = (uint8_t*)(w + l.q8);
+  p.k8 = (uint8_t*)(w + l.k8);
+  p.v8t = (uint8_t*)(w + l.v8t);
+  p.sq = (float*)(w + l.sq);
+  p.sk = (float*)(w + l.sk);
+  p.sv = (float*)(w + l.sv);
+  p.BH = B * H;
+  p.N = N;
+  p.n_t64 = (N + 63) / 64;
+  p.Npad = 64 * p.n_t64;
+  p.mask_tiles = (N + fa::MASK_TILE - 1) / fa::MASK_TILE;
+  p.scale_log2e = scale * kLog2e;
+  p.rsqrt_d = 1.0f / std::sqrt((float)d);
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -156,6 +206,37 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
   p.scale = scale;
   p.scale_log2e = scale * kLog2e;
   const hipError_t e = fa::launch_backward(p, dtype, d, causal != 0, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_forward_fp8_workspace_size(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
+  return fp8_layout(B, H, N, d).total;
+}
+
+int fa_fp8_prepare(const void* q, const void* k, const void* v, int B, int H, int N, int d,
+                   int dtype, const int8_t* signs, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  fa::Fp8Params p{};
+  const int rc = fp8_setup(p, q, k, v, B, H, N, d, 1.0f, dtype, signs, workspace, workspace_bytes);
+  if (rc != FA_OK) return rc;
+  const hipError_t e = fa::launch_fp8(p, dtype, d, false, true, false, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_forward_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const uint8_t* block_mask, int dtype, const int8_t* signs,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (!tensor_ptr_ok(o) || lse == nullptr || !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
+  fa::Fp8Params p{};
+  const int rc = fp8_setup(p, q, k, v, B, H, N, d, scale, dtype, signs, workspace, workspace_bytes);
+  if (rc != FA_OK) return rc;
+  if (block_mask != nullptr && p.mask_tiles > fa::FWD_MAX_MASK_TILES) return FA_ERR_UNSUPPORTED;
+  p.o = o;
+  p.lse = lse;
+  p.mask = block_mask;
+  const hipError_t e = fa::launch_fp8(p, dtype, d, causal != 0, true, true, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

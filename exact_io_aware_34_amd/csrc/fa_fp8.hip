@@ -1,0 +1,457 @@
+// FP8 forward pass with incoherent processing on gfx950.
+//
+// The method (marketmaker.cc page, section "FA3 : Mécanique de la trémie",
+// point 3): FP8 attention is ruined by outliers unless the vectors are first
+// rotated randomly, which spreads an outlier's magnitude over every
+// coordinate, and then quantised per block.  The rotation here is
+// R = diag(sigma) H_d / sqrt(d) (Sylvester-Hadamard H_d, random signs sigma
+// passed in by the caller); R is orthogonal, so (Q R)(K R)^T = Q K^T.  Q and
+// K rows are rotated, V is not.  Every 64-row block of the rotated Q, of the
+// rotated K and of V gets one fp32 scale s = amax / 448 (448 is the largest
+// E4M3 value) and becomes E4M3(x * 448 / amax).  The attention itself is the
+// online-softmax forward of the 16-bit path ("Método", xyznot.com reading
+// guide) on E4M3 operands: scores S = scale * s_q s_k (Q8 K8^T) accumulate in
+// fp32 on the matrix cores, the softmax statistics stay fp32, and P is
+// rounded to E4M3 for the P V product after the value block's scale ratio
+// r_t = s_v[t] / max_t s_v[t] is folded into it, so that
+// O = max_t s_v[t] * sum_j E4M3(P_ij r_t) V8_j / l_i.
+//
+// Two kernels:
+//   * fp8_prep_kernel: one workgroup per (Q, K or V; batch*head; 64-row
+//     block).  Four lanes hold one row; the Walsh-Hadamard transform runs as
+//     in-lane butterflies plus two DPP stages across the four lanes.  Q8 and
+//     K8 are written row-major (rows padded to a multiple of 64 with zeros);
+//     V8 is written transposed per 64-key block, [d][64], with the keys of a
+//     block permuted so that each lane's slice of a row is exactly the 32
+//     keys it multiplies in the P V product.
+//   * fwd8_kernel: the 16-bit forward's grid and causal / block-sparse tile
+//     skipping, 64-key K and V^T tiles in a three-slot LDS ring filled by
+//     direct global->LDS copies, S^T = K Q^T and O^T += V^T P^T on
+//     v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, neutral block scales,
+//     fp32 accumulation).  Lane l holds query l % 32 at 16 keys of each
+//     32-key unit, which are exactly its 32 contraction slots of the P V
+//     product over the tile's 64 keys: P goes from the score accumulators to
+//     the operand with no shuffle.
+#include <type_traits>
+
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+namespace fa {
+
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kE4M3Max = 448.f;
+
+__device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c) {
+  // Formats 0/0: both operands E4M3; scale operands 127 = 2^0 (E8M0).
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Four fp32 values to four E4M3 bytes (a in the lowest byte).  The
+// conversion rounds to nearest even; it does not saturate, so every caller
+// keeps |x| <= 448.
+__device__ __forceinline__ int pack_e4m3(float a, float b, float c, float d) {
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false), true);
+}
+
+__device__ __forceinline__ float quad_xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float quad_xor2(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+}
+
+// XOR swizzle of 16-byte chunks in LDS tiles with rows of RB bytes, for
+// reads of 16 consecutive rows at one chunk per pass.
+template <int RB>
+__device__ __forceinline__ int swz8(int r) {
+  if constexpr (RB == 64) return (r >> 2) & 3;
+  else return (r >> 1) & 7;
+}
+
+// Key (within a 64-key block) held at position p of the transposed V block:
+// position 32 g + e is the e-th contraction slot of lanes g = l / 32.
+__device__ __forceinline__ int vt_key(int pos) {
+  const int g = pos >> 5, e = pos & 31;
+  return 32 * (e >> 4) + 8 * ((e & 15) >> 2) + 4 * g + (e & 3);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8Params p) {
+  using VT = typename V8<T>::t;
+  constexpr int EPT = D / 4;        // elements per lane (four lanes per row)
+  __shared__ float red[4];
+  __shared__ __attribute__((aligned(16))) uint8_t vtile[64 * D];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int z = blockIdx.y;         // 0 = Q, 1 = K, 2 = V
+  const int nt = p.n_t64;
+  const int bh = blockIdx.x / nt, t = blockIdx.x - bh * nt;
+  const int row = tid >> 2, qd = tid & 3;
+  const int N = p.N;
+  const int key = t * 64 + row;
+  const T* src = (const T*)(z == 0 ? p.q : (z == 1 ? p.k : p.v));
+
+  float x[EPT];
+  if (key < N) {
+    const T* rp = src + ((size_t)bh * N + key) * D + qd * EPT;
+#pragma unroll
+    for (int c = 0; c < EPT / 8; ++c) {
+      const VT v8 = *(const VT*)(rp + 8 * c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[8 * c + e] = (float)v8[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) x[e] = 0.f;
+  }
+
+  if (z < 2 && p.signs != nullptr) {
+    // x <- (x * sigma) H_d / sqrt(d); element index = qd * EPT + e, so the
+    // low bits of the index are in-lane and the two high bits are qd.
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+      if (p.signs[qd * EPT + e] < 0) x[e] = -x[e];
+#pragma unroll
+    for (int h = 1; h < EPT; h *= 2)
+#pragma unroll
+      for (int i = 0; i < EPT; ++i)
+        if ((i & h) == 0) {
+          const float a = x[i], b = x[i + h];
+          x[i] = a + b;
+          x[i + h] = a - b;
+        }
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const float y = quad_xor1(x[e]);
+      x[e] = (qd & 1) ? y - x[e] : x[e] + y;
+    }
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const float y = quad_xor2(x[e]);
+      x[e] = (qd & 2) ? y - x[e] : x[e] + y;
+    }
+    const float rs = p.rsqrt_d;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) x[e] *= rs;
+  }
+
+  // Block amax over the 64 rows.
+  float am = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) am = fmaxf(am, fabsf(x[e]));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+  if (lane == 0) red[wave] = am;
+  __syncthreads();
+  am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float inv = am > 0.f ? kE4M3Max / am : 1.f;
+  if (tid == 0) {
+    float* sc = z == 0 ? p.sq : (z == 1 ? p.sk : p.sv);
+    sc[(size_t)bh * nt + t] = am > 0.f ? am / kE4M3Max : 1.f;
+  }
+
+  int w[EPT / 4];
+#pragma unroll
+  for (int i = 0; i < EPT / 4; ++i) {
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = fminf(fmaxf(x[4 * i + e] * inv, -kE4M3Max), kE4M3Max);
+    w[i] = pack_e4m3(y[0], y[1], y[2], y[3]);
+  }
+  if (z < 2) {
+    uint8_t* dst = (z == 0 ? p.q8 : p.k8) + ((size_t)bh * p.Npad + key) * D + qd * EPT;
+#pragma unroll
+    for (int i = 0; i < EPT / 16; ++i)
+      *(i32x4*)(dst + 16 * i) = i32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+    return;
+  }
+  // V: transpose the block through LDS into [d][64 positions].
+#pragma unroll
+  for (int i = 0; i < EPT / 4; ++i) *(int*)(vtile + row * D + qd * EPT + 4 * i) = w[i];
+  __syncthreads();
+  constexpr int OB = D * 64 / 256;  // output bytes per thread
+  uint8_t* dst = p.v8t + ((size_t)bh * nt + t) * (64 * D) + tid * OB;
+#pragma unroll
+  for (int i = 0; i < OB / 16; ++i) {
+    int ov[4];
+#pragma unroll
+    for (int dw = 0; dw < 4; ++dw) {
+      unsigned acc = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int o = tid * OB + 16 * i + 4 * dw + b;
+        const int d = o >> 6, pos = o & 63;
+        acc |= (unsigned)vtile[vt_key(pos) * D + d] << (8 * b);
+      }
+      ov[dw] = (int)acc;
+    }
+    *(i32x4*)(dst + 16 * i) = i32x4{ov[0], ov[1], ov[2], ov[3]};
+  }
+}
+
+template <typename T, int D, bool CAUSAL, bool SPARSE>
+__global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
+  using HT = typename V8<T>::h;
+  constexpr int NW = 4, BR = 128, BC = 64, NS = 3;
+  constexpr int TB = BC * D;                 // bytes of a K tile (and of a V^T tile)
+  constexpr int DH = D / 64;                 // score MFMAs per 32-key unit
+  constexpr int DB = D / 32;                 // O^T row blocks
+  constexpr int CPR = D / 16;                // 16-byte chunks per K row
+  constexpr int DMA_N = TB / 16 / 256;       // copies per wave per tile
+  static_assert(BR == MASK_TILE, "a workgroup covers one block-mask row");
+  __shared__ __attribute__((aligned(1024))) uint8_t kvs[2 * NS * TB];  // K slots, then V^T slots
+  __shared__ uint8_t mask_s[SPARSE ? FWD_MAX_MASK_TILES : 1];
+  __shared__ float red_s[4];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+  const int N = p.N, nt = p.n_t64;
+  const int n_qt = (N + BR - 1) / BR;
+  int bh, qt;
+  if (CAUSAL) {
+    bh = blockIdx.x % p.BH;
+    qt = n_qt - 1 - blockIdx.x / p.BH;
+  } else {
+    const int lid = xcd_remap(blockIdx.x, n_qt * p.BH);
+    bh = lid / n_qt;
+    qt = lid - bh * n_qt;
+  }
+  const uint8_t* __restrict__ K8 = p.k8 + (size_t)bh * p.Npad * D;
+  const uint8_t* __restrict__ V8 = p.v8t + (size_t)bh * nt * TB;
+  const float* __restrict__ skh = p.sk + (size_t)bh * nt;
+  const float* __restrict__ svh = p.sv + (size_t)bh * nt;
+  const int q0w = qt * BR + wave * 32;
+
+  if (SPARSE)
+    for (int i = tid; i < p.mask_tiles; i += 256) mask_s[i] = p.mask[(size_t)qt * p.mask_tiles + i];
+  // Largest value-block scale of this head.
+  float mv = 0.f;
+  for (int i = tid; i < nt; i += 256) mv = fmaxf(mv, svh[i]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mv = fmaxf(mv, __shfl_xor(mv, off));
+  if (lane == 0) red_s[wave] = mv;
+  __syncthreads();
+  const float sv_max = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
+
+  // Per-lane LDS byte offsets.  K (A operand of S^T): key 32 u + l32, bytes
+  // 64 h + 32 g .. + 31.  V^T (A operand of O^T): row 32 db + l32, bytes
+  // 32 g .. + 31 (positions = the lane's contraction slots).
+  int koff[2][DH][2], voff[DB][2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int h = 0; h < DH; ++h)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int r = 32 * u + l32, ch = 4 * h + 2 * g + c;
+        koff[u][h][c] = r * D + 16 * (ch ^ swz8<D>(r));
+      }
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int r = 32 * db + l32, ch = 2 * g + c;
+      voff[db][c] = TB * NS + r * 64 + 16 * (ch ^ swz8<64>(r));
+    }
+  // Copy schedule: copy u of this wave fills physical chunk pch of a tile.
+  uint32_t kdo[DMA_N], vdo[DMA_N];
+#pragma unroll
+  for (int u = 0; u < DMA_N; ++u) {
+    const int pch = (u * NW + wave) * 64 + lane;
+    const int kr = pch / CPR, kc = (pch % CPR) ^ swz8<D>(kr);
+    kdo[u] = (uint32_t)(kr * D + 16 * kc);
+    const int vr = pch >> 2, vc = (pch & 3) ^ swz8<64>(vr);
+    vdo[u] = (uint32_t)(vr * 64 + 16 * vc);
+  }
+  const uint32_t lds0 = lds_addr(kvs);
+
+  const int n_kt = (N + BC - 1) / BC;
+  int kt_end = n_kt;
+  if (CAUSAL) kt_end = min(kt_end, (min(N, (qt + 1) * BR) + BC - 1) / BC);
+  auto next_active = [&](int jj) {
+    if (SPARSE)
+      while (jj < kt_end && mask_s[(jj * BC) / MASK_TILE] == 0) ++jj;
+    return jj;
+  };
+  const int last_key = CAUSAL ? min(N - 1, q0w + 31) : N - 1;
+  const int plain_key = CAUSAL ? min(N - 1, q0w) : N - 1;
+
+  // Copy K tile jj and V^T tile jj into slot `slot` (rows past N are zero
+  // in both: the preparation pads them).
+  auto issue = [&](int jj, int slot) {
+    const uint8_t* ks = K8 + (size_t)jj * TB;
+    const uint8_t* vs = V8 + (size_t)jj * TB;
+    const uint32_t kd = lds0 + (uint32_t)(slot * TB), vd = lds0 + (uint32_t)((NS + slot) * TB);
+#pragma unroll
+    for (int u = 0; u < DMA_N; ++u) dma16_s(ks, kdo[u], kd + (uint32_t)((u * NW + wave) * 1024));
+#pragma unroll
+    for (int u = 0; u < DMA_N; ++u) dma16_s(vs, vdo[u], vd + (uint32_t)((u * NW + wave) * 1024));
+  };
+
+  int jq[NS];
+  jq[0] = next_active(0);
+  jq[1] = jq[0] < kt_end ? next_active(jq[0] + 1) : kt_end;
+  jq[2] = jq[1] < kt_end ? next_active(jq[1] + 1) : kt_end;
+  if (jq[0] < kt_end) issue(jq[0], 0);
+  if (jq[1] < kt_end) issue(jq[1], 1);
+
+  // Q^T (B operand): lane holds query q0w + l32, bytes 64 h + 32 g .. + 31.
+  i32x8 qf[DH];
+  {
+    const int q = q0w + l32;
+#pragma unroll
+    for (int h = 0; h < DH; ++h)
+      qf[h] = q < N ? *(const i32x8*)(p.q8 + ((size_t)bh * p.Npad + q) * D + 64 * h + 32 * g)
+                    : i32x8{};
+  }
+  const float sq_w = p.sq[(size_t)bh * nt + min(q0w, N - 1) / 64];
+  wait_all_loads();
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  float m_run = -1e30f;   // running reference, log2 units of the scaled score
+  float l_run = 0.f;      // this lane's share of sum exp2(x - m_run)
+  const float c0 = p.scale_log2e * sq_w;
+
+  int slot = 0;
+  while (jq[0] < kt_end) {
+    const int j = jq[0];
+    if (jq[1] < kt_end) wait_vmcnt<2 * DMA_N>();
+    else wait_vmcnt<0>();
+    wg_barrier();
+    if (jq[2] < kt_end) issue(jq[2], slot == 0 ? 2 : slot - 1);
+    if (j * BC <= last_key) {
+      const uint8_t* kt = kvs + slot * TB;
+      const uint8_t* vt = kvs + slot * TB;   // V^T offsets already include NS * TB
+      f32x16 s[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        s[u] = f32x16{};
+#pragma unroll
+        for (int h = 0; h < DH; ++h) {
+          const i32x4 lo = *(const i32x4*)(kt + koff[u][h][0]);
+          const i32x4 hi = *(const i32x4*)(kt + koff[u][h][1]);
+          const i32x8 kf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          s[u] = mfma_f8(kf, qf[h], s[u]);
+        }
+      }
+      // Scores past this lane's last visible key become -inf.
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int ks = j * BC + 32 * u;
+        if (ks + 31 > plain_key) {
+          const int lim = min(N - 1, CAUSAL ? q0w + l32 : N - 1) - ks - 4 * g;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (8 * (r >> 2) + (r & 3) > lim) s[u][r] = -INFINITY;
+        }
+      }
+      const float cj = c0 * skh[j];                       // raw accumulator -> log2 units
+      const float inv_r = sv_max / svh[j];                // 1 / r_t
+      const float lr = __log2f(svh[j] / sv_max);          // log2 r_t <= 0
+      i32x8 pk;
+      // p' = exp2(x - m_run) * r_t, packed to E4M3; returns the lane's sum of p'.
+      auto exps = [&]() {
+        const float off = lr - m_run;
+        float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int w4 = 0; w4 < 4; ++w4) {
+            float e[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) e[b] = fast_exp2(fmaf(s[u][4 * w4 + b], cj, off));
+            ls0 += e[0] + e[1];
+            ls1 += e[2] + e[3];
+            pk[4 * u + w4] = pack_e4m3(e[0], e[1], e[2], e[3]);
+          }
+        return ls0 + ls1;
+      };
+      float ls = exps();
+      // The reference moves only when some lane's tile sum exceeds 2^8 (so
+      // every packed value stays below 448); O, l and lse share it.
+      if (wave_any(!(ls <= 256.f))) {
+        float mx = s[0][0];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[u][r]);
+        const float m_new = fmaxf(m_run, half_swap_max(mx * cj));
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        ls = exps();
+      }
+      l_run = fmaf(ls, inv_r, l_run);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const i32x4 lo = *(const i32x4*)(vt + voff[db][0]);
+        const i32x4 hi = *(const i32x4*)(vt + voff[db][1]);
+        o[db] = mfma_f8(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pk, o[db]);
+      }
+    }
+    jq[0] = jq[1];
+    jq[1] = jq[2];
+    jq[2] = jq[1] < kt_end ? next_active(jq[1] + 1) : kt_end;
+    slot = slot == NS - 1 ? 0 : slot + 1;
+  }
+
+  // Epilogue: O = sv_max * O / l, lse = (m + log2 l) * ln 2.
+  const float lt = half_swap_sum(l_run);
+  const float inv = lt > 0.f ? sv_max / lt : 0.f;
+  const int q = q0w + l32;
+  if (q < N) {
+    T* orow = (T*)p.o + ((size_t)bh * N + q) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        HT hv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hv[e] = (T)(o[db][4 * rg + e] * inv);
+        *(HT*)(orow + 32 * db + 8 * rg + 4 * g) = hv;
+      }
+    if (g == 0)
+      p.lse[(size_t)bh * N + q] = lt > 0.f ? (m_run + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_fp8_t(const Fp8Params& p, bool causal, bool sparse, bool prep, bool attend,
+                        hipStream_t st) {
+  if (prep) {
+    hipLaunchKernelGGL((fp8_prep_kernel<T, D>), dim3((unsigned)(p.BH * p.n_t64), 3), dim3(256), 0,
+                       st, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !attend) return e;
+  }
+  const dim3 grid((unsigned)(((p.N + 127) / 128) * p.BH)), block(256);
+  if (causal && sparse) hipLaunchKernelGGL((fwd8_kernel<T, D, true, true>), grid, block, 0, st, p);
+  else if (causal) hipLaunchKernelGGL((fwd8_kernel<T, D, true, false>), grid, block, 0, st, p);
+  else if (sparse) hipLaunchKernelGGL((fwd8_kernel<T, D, false, true>), grid, block, 0, st, p);
+  else hipLaunchKernelGGL((fwd8_kernel<T, D, false, false>), grid, block, 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fp8(Fp8Params p, int dtype, int d, bool causal, bool prep, bool attend,
+                      hipStream_t st) {
+  const bool sparse = p.mask != nullptr;
+  if (dtype == DT_BF16)
+    return d == 64 ? launch_fp8_t<__bf16, 64>(p, causal, sparse, prep, attend, st)
+                   : launch_fp8_t<__bf16, 128>(p, causal, sparse, prep, attend, st);
+  return d == 64 ? launch_fp8_t<_Float16, 64>(p, causal, sparse, prep, attend, st)
+                 : launch_fp8_t<_Float16, 128>(p, causal, sparse, prep, attend, st);
+}
+
+}  // namespace fa

@@ -26,6 +26,9 @@ constexpr int bwd_u_waves(int d) { return d == 64 ? 2 : 1; }
 constexpr int dec_waves(int d) { return d == 64 ? 2 : 1; }
 constexpr int DEC_MAX_NQ = 16;  // queries per head the decode kernel holds (one MFMA column block)
 constexpr int DEC_SPLIT_ALIGN = 128;  // key-range lengths are multiples of 4 waves x 32 keys
+// FP8 forward: waves per SIMD (three-slot rings of 64-key E4M3 K and V^T
+// tiles: 24 KiB at d = 64, 48 KiB at d = 128).
+constexpr int fwd8_waves(int d) { return d == 64 ? 3 : 2; }
 constexpr int FWD_MAX_MASK_TILES = 2048;  // block-mask columns the forward caches (N <= 262144)
 
 struct FwdParams {
@@ -72,8 +75,31 @@ struct DecParams {
   float scale_log2e;
 };
 
+struct Fp8Params {
+  const void* q;  // (B*H, N, d) 16-bit inputs
+  const void* k;
+  const void* v;
+  void* o;        // (B*H, N, d), dtype of q
+  float* lse;     // (B*H, N)
+  const int8_t* signs;  // d random signs of the rotation, nullptr = no rotation
+  // Prepared operands (workspace): Q8, K8 (B*H, Npad, d) E4M3 row-major;
+  // V8^T (B*H, n_t64, d, 64) E4M3, keys of a block permuted; one fp32 scale
+  // per (b*h, 64-row block) of each.
+  uint8_t* q8;
+  uint8_t* k8;
+  uint8_t* v8t;
+  float* sq;
+  float* sk;
+  float* sv;
+  const uint8_t* mask;  // nullptr = dense
+  int BH, N, Npad, n_t64, mask_tiles;
+  float scale_log2e, rsqrt_d;
+};
+
 hipError_t launch_forward(FwdParams p, int dtype, int d, bool causal, hipStream_t st);
 hipError_t launch_backward(BwdParams p, int dtype, int d, bool causal, hipStream_t st);
 hipError_t launch_decode(DecParams p, int dtype, int d, bool causal, hipStream_t st);
+hipError_t launch_fp8(Fp8Params p, int dtype, int d, bool causal, bool prep, bool attend,
+                      hipStream_t st);
 
 }  // namespace fa

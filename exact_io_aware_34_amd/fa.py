@@ -9,6 +9,7 @@ library has not been built (there is no other code path).
     o, lse = fa.forward(q, k, v, causal=True)
     dq, dk, dv = fa.backward(q, k, v, o, lse, do, causal=True)
     o, lse = fa.decode(q_new, k_cache, v_cache)        # Nq <= 16 queries, Nk keys
+    o, lse = fa.forward_fp8(q, k, v, signs=signs, causal=True)   # E4M3 operands
 """
 
 import ctypes
@@ -37,6 +38,13 @@ _lib.fa_decode_splits.argtypes = [_i, _i, _i, _i, _i, _i]
 _lib.fa_decode_splits.restype = _i
 _lib.fa_decode_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i]
 _lib.fa_decode_workspace_size.restype = ctypes.c_size_t
+_lib.fa_forward_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _i, _vp, _vp,
+                                ctypes.c_size_t, _vp]
+_lib.fa_forward_fp8.restype = _i
+_lib.fa_fp8_prepare.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.fa_fp8_prepare.restype = _i
+_lib.fa_forward_fp8_workspace_size.argtypes = [_i, _i, _i, _i]
+_lib.fa_forward_fp8_workspace_size.restype = ctypes.c_size_t
 _lib.fa_status_string.argtypes = [_i]
 _lib.fa_status_string.restype = ctypes.c_char_p
 _lib.fa_abi_version.restype = _i
@@ -185,6 +193,70 @@ def decode(q, k, v, causal=False, scale=None, n_splits=0, out=None, lse=None, wo
     rc = _lib.fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, scale,
                         int(bool(causal)), int(n_splits), DTYPE_CODES[q.dtype], _ptr(workspace),
                         nbytes, _stream(stream))
+    if rc != 0:
+        raise FAError(rc)
+    return o, lse
+
+
+def fp8_workspace_size(B, H, N, d) -> int:
+    return int(_lib.fa_forward_fp8_workspace_size(B, H, N, d))
+
+
+def _fp8_args(q, k, v, signs, workspace):
+    _check_inputs(q, k, v)
+    B, H, N, d = q.shape
+    if signs is not None:
+        if signs.dtype != torch.int8 or tuple(signs.shape) != (d,) or not signs.is_cuda:
+            raise ValueError(f"signs must be an int8 GPU tensor of shape ({d},)")
+    ws_bytes = fp8_workspace_size(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    return workspace
+
+
+def fp8_prepare(q, k, v, signs=None, workspace=None, stream=None):
+    """Rotation + block quantisation only; returns the filled workspace."""
+    workspace = _fp8_args(q, k, v, signs, workspace)
+    B, H, N, d = q.shape
+    rc = _lib.fa_fp8_prepare(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, DTYPE_CODES[q.dtype],
+                             _ptr(signs), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(stream))
+    if rc != 0:
+        raise FAError(rc)
+    return workspace
+
+
+def fp8_views(workspace, B, H, N, d):
+    """Views of the workspace regions in the layout fa.h documents:
+    (q8, k8, v8t) as uint8 and (s_q, s_k, s_v) as float32."""
+    nt = -(-N // 64)
+    pad = lambda b: -(-b // 256) * 256  # noqa: E731
+    op, sc = pad(B * H * nt * 64 * d), pad(B * H * nt * 4)
+    ws = workspace.view(torch.uint8)
+    q8 = ws[0:B * H * nt * 64 * d].view(B, H, nt * 64, d)
+    k8 = ws[op:op + B * H * nt * 64 * d].view(B, H, nt * 64, d)
+    v8t = ws[2 * op:2 * op + B * H * nt * 64 * d].view(B, H, nt, d, 64)
+    scales = [ws[3 * op + i * sc:3 * op + i * sc + B * H * nt * 4].view(torch.float32).view(B, H, nt)
+              for i in range(3)]
+    return (q8, k8, v8t), tuple(scales)
+
+
+def forward_fp8(q, k, v, signs=None, causal=False, scale=None, block_mask=None, out=None,
+                lse=None, workspace=None, stream=None):
+    """FP8 forward with incoherent processing: returns (o, lse) like forward()."""
+    workspace = _fp8_args(q, k, v, signs, workspace)
+    B, H, N, d = q.shape
+    scale = default_scale(d) if scale is None else float(scale)
+    mask = _mask_arg(block_mask, N)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_inputs(q, o)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 (B, H, N)")
+    rc = _lib.fa_forward_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, scale,
+                             int(bool(causal)), _ptr(mask), DTYPE_CODES[q.dtype], _ptr(signs),
+                             _ptr(workspace), workspace.numel() * workspace.element_size(),
+                             _stream(stream))
     if rc != 0:
         raise FAError(rc)
     return o, lse

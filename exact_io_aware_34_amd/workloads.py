@@ -201,3 +201,21 @@ def draw_decode(B, H, Nq, Nk, d, dtype="bf16", seed=0, device="cpu"):
             k[b, h].copy_(hk)
             v[b, h].copy_(hv)
     return q, k, v
+
+
+def draw_rotation_signs(d, seed):
+    """The d random signs (+1 / -1, int8) of the FP8 path's rotation."""
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randint(0, 2, (d,), generator=g, dtype=torch.int8) * 2 - 1).to(torch.int8)
+
+
+def draw_outlier_qkv(B, H, N, d, dtype="bf16", seed=0, frac=1e-3, sd=10.0):
+    """N(0, 1) q, k, v with a fraction `frac` of the q and k entries redrawn
+    from N(0, sd^2): the outliers that FP8 quantisation handles badly."""
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((3, B, H, N, d), generator=g, dtype=torch.float32)
+    for i in (0, 1):
+        m = torch.rand((B, H, N, d), generator=g) < frac
+        x[i][m] = torch.randn((int(m.sum()),), generator=g) * sd
+    x = x.to(TORCH_DTYPES[dtype])
+    return tuple(x.unbind(0))

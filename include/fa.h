@@ -141,6 +141,59 @@ int fa_decode_splits(int B, int H, int Nq, int Nk, int d, int n_splits);
  * each array padded to 256 bytes. */
 size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d, int n_splits);
 
+/*
+ * FP8 forward with incoherent processing.
+ *
+ * FP8 attention is ruined by outliers unless the vectors are first rotated
+ * randomly, spreading an outlier's magnitude over every coordinate, and then
+ * quantised per block ("Attention flash et question de longueur de
+ * séquence", marketmaker.cc, section "FA3 : Mécanique de la trémie", point
+ * 3).  Here:
+ *   rotation      R = diag(signs) H_d / sqrt(d), H_d the Sylvester-Hadamard
+ *                 matrix; Q and K rows are multiplied by R (Q K^T is
+ *                 unchanged), V is not;
+ *   quantisation  every 64-row block of R-rotated Q, of R-rotated K and of V:
+ *                 scale s = amax / 448 (1 for an all-zero block), codes
+ *                 E4M3(x * 448 / amax) (OCP E4M3, round to nearest even);
+ *   attention     S = scale * s_q s_k (Q8 K8^T) with fp32 accumulation on the
+ *                 FP8 matrix cores, fp32 online softmax (running max m, sum l),
+ *                 P rounded to E4M3 after the value block's scale ratio
+ *                 r_t = s_v[t] / max_t s_v[t] is folded into it,
+ *                 O = max_t s_v[t] * sum_j E4M3(P_ij r_t) V8_j / l_i,
+ *                 lse = m + ln l.
+ * The result approximates exact attention to FP8 precision (a few percent
+ * of |O| on N(0, 1) inputs); it is not exact.
+ *
+ * q, k, v: (B,H,N,d) FA_BF16 or FA_F16; o: same shape and dtype; lse: (B,H,N)
+ * fp32.  `signs`: device pointer to d int8 values (negative = -1, otherwise
+ * +1), the random signs of the rotation, drawn by the caller; NULL skips the
+ * rotation (block-quantised FP8 without incoherent processing).  causal and
+ * block_mask as for fa_forward.  `workspace` (at least
+ * fa_forward_fp8_workspace_size() bytes, 256-byte aligned, caller-owned)
+ * receives the prepared operands, in this order, each region padded to 256
+ * bytes, with nt = ceil(N / 64) and Npad = 64 nt:
+ *   Q8  (B*H, Npad, d) E4M3 codes, row-major (rows >= N are zero)
+ *   K8  (B*H, Npad, d) E4M3 codes
+ *   V8T (B*H, nt, d, 64) E4M3 codes of each 64-key block transposed, position
+ *       32 g + e holding key 32 (e / 16) + 8 ((e % 16) / 4) + 4 g + e % 4 of
+ *       the block (keys >= N are zero)
+ *   s_q, s_k, s_v (B*H, nt) fp32 block scales.
+ * Supported: d in {64, 128}; FA_F32 -> FA_ERR_UNSUPPORTED.
+ */
+int fa_forward_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const uint8_t* block_mask, int dtype, const int8_t* signs,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* The rotation and quantisation step of fa_forward_fp8 alone: fills the
+ * workspace regions Q8, K8, V8T, s_q, s_k, s_v described above. */
+int fa_fp8_prepare(const void* q, const void* k, const void* v, int B, int H, int N, int d,
+                   int dtype, const int8_t* signs, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* Bytes of workspace fa_forward_fp8 and fa_fp8_prepare need (0 on bad input). */
+size_t fa_forward_fp8_workspace_size(int B, int H, int N, int d);
+
 /* Static, human-readable text for a status code. */
 const char* fa_status_string(int status);
 

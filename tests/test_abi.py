@@ -31,19 +31,25 @@ def lib():
     L.fa_decode_splits.argtypes = [i] * 6
     L.fa_decode_workspace_size.argtypes = [i] * 6
     L.fa_decode_workspace_size.restype = ctypes.c_size_t
+    L.fa_forward_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, vp,
+                                 ctypes.c_size_t, vp]
+    L.fa_fp8_prepare.argtypes = [vp, vp, vp, i, i, i, i, i, vp, vp, ctypes.c_size_t, vp]
+    L.fa_forward_fp8_workspace_size.argtypes = [i, i, i, i]
+    L.fa_forward_fp8_workspace_size.restype = ctypes.c_size_t
     return L
 
 
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "fa_abi_version", "fa_backward", "fa_backward_workspace_size", "fa_decode",
-        "fa_decode_splits", "fa_decode_workspace_size", "fa_forward", "fa_status_string"])
+        "fa_decode_splits", "fa_decode_workspace_size", "fa_forward", "fa_forward_fp8",
+        "fa_forward_fp8_workspace_size", "fa_fp8_prepare", "fa_status_string"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -164,3 +170,33 @@ def test_decode_validation(lib):
     assert dec(lib, ws=None) == -3
     need = lib.fa_decode_workspace_size(1, 2, 1, 1000, 64, 4)
     assert need > 0 and dec(lib, ws_bytes=need - 1) == -3
+
+
+def test_fp8_workspace_size(lib):
+    W = lib.fa_forward_fp8_workspace_size
+    # 3 operand regions of B*H*Npad*d bytes + 3 scale regions of B*H*nt fp32, each padded to 256
+    assert W(4, 12, 8192, 64) == 3 * 48 * 8192 * 64 + 3 * 48 * 128 * 4
+    assert W(1, 1, 65, 128) == 3 * 128 * 128 + 3 * 256
+    assert W(0, 1, 64, 64) == 0
+
+
+def f8(lib, q=FAKE, o=FAKE, lse=FAKE, N=100, d=64, dtype=2, ws=FAKE, ws_bytes=1 << 30,
+       scale=0.125):
+    return lib.fa_forward_fp8(q, FAKE, FAKE, o, lse, 2, 3, N, d, scale, 1, None, dtype, None, ws,
+                              ws_bytes, None)
+
+
+def test_fp8_validation(lib):
+    assert f8(lib, q=None) == -1
+    assert f8(lib, o=MISALIGNED) == -1
+    assert f8(lib, lse=None) == -1
+    assert f8(lib, N=0) == -1
+    assert f8(lib, scale=0.0) == -1
+    assert f8(lib, d=96) == -2
+    assert f8(lib, dtype=0) == -2                       # fp32 inputs not built
+    assert f8(lib, ws=None) == -3
+    assert f8(lib, ws=ctypes.c_void_p((1 << 20) + 16)) == -3   # not 256-byte aligned
+    need = lib.fa_forward_fp8_workspace_size(2, 3, 100, 64)
+    assert f8(lib, ws_bytes=need - 1) == -3
+    assert lib.fa_fp8_prepare(FAKE, FAKE, FAKE, 2, 3, 100, 64, 2, None, None, 0, None) == -3
+    assert lib.fa_fp8_prepare(None, FAKE, FAKE, 2, 3, 100, 64, 2, None, FAKE, need, None) == -1
