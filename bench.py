@@ -1,7 +1,7 @@
 """Throughput of exact attention forward + backward on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                [--calibrate-copy] [--decode-workload NAME | --no-decode]
+                [--calibrate-copy] [--decode-workload NAME | --no-decode] [--no-fp8]
 
 A step is one forward pass and one backward pass (every kernel of the path:
 forward, backward preprocess, backward main) over the workload's synthetic
@@ -15,6 +15,13 @@ is timed after the steps on its own workload and reported in the `decode`
 object of the same line: call time, algorithmic HBM bytes per call (16-bit K
 and V read once, q read, o and lse written) over that time against the
 8 TB/s HBM peak, and the oracle's rate on a few heads.
+
+The FP8 forward (fa_forward_fp8: rotation + block quantisation, then
+attention on E4M3 operands) is timed on the same workload and reported in the
+`fp8` object: call time (both kernels) and the preparation alone, the
+workload's forward FLOPs (same count as the 16-bit forward) over the call
+time against the 5.0 PFLOP/s dense FP8 peak, and the oracle's float64
+emulation of the method on a sample of heads.
 
 `roofline.traffic` comes from profiles/hbm_traffic_<workload>.json (FETCH_SIZE
 and WRITE_SIZE counter runs of this script, scaled by the same counters on a
@@ -35,7 +42,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X dense, published
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3, "fp8": 5000.0}   # MI355X dense, published
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd/bwd TFLOPS (bf16, N=8192, d=64, causal) and % of MFMA peak"
 
@@ -52,6 +59,8 @@ def parse():
     ap.add_argument("--decode-workload", default="decode_b8h12_q1_k65536_d64_bf16")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-cpu-heads", type=int, default=24)
+    ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--fp8-cpu-heads", type=int, default=2)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB device-to-device copy before the steps "
                          "(reference kernel for HBM byte counters)")
@@ -242,6 +251,77 @@ def bench_decode(fa, name, steps, warmup, cpu_heads, with_cpu):
     return out
 
 
+def fp8_cpu_baseline(w, inputs, signs, n_heads):
+    """The oracle's float64 emulation of the FP8 forward on `n_heads` heads
+    (query rows in chunks of 1024), as equivalent TFLOP/s."""
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)][:n_heads]
+    sg = signs.numpy().astype("float64")
+    t = 0.0
+    for b, h in heads:
+        a = [inputs[n][b, h].double().numpy() for n in ("q", "k", "v")]
+        for r0 in range(0, w.N, 1024):
+            rows = list(range(r0, min(w.N, r0 + 1024)))
+            t0 = time.perf_counter()
+            oracle.fp8_forward_head(*a, w.scale, w.causal, None, sg, rows=rows)
+            t += time.perf_counter() - t0
+    f_fwd, _ = flops(w, inputs["mask"])
+    per_head = f_fwd / (w.B * w.H)
+    threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+    return {"value": round(per_head * len(heads) / t / 1e12, 5), "unit": "TFLOPS", "cores": threads,
+            "kind": "oracle", "seconds": round(t, 3),
+            "sample": f"{len(heads)} of {w.B * w.H} heads, float64 emulation of the FP8 method "
+                      f"(operands quantised whole, query rows in chunks of 1024), "
+                      f"os.cpu_count()={os.cpu_count()}"}
+
+
+def bench_fp8(fa, w, inputs, tensors, mask, steps, warmup, cpu_heads, with_cpu):
+    import torch
+
+    from exact_io_aware_34_amd import workloads as W
+    q, k, v, _, o, lse, _, _ = tensors
+    signs = W.draw_rotation_signs(w.d, seed=7)
+    sd = signs.to(q.device)
+    ws = torch.empty(fa.fp8_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+    call = timed(lambda: fa.forward_fp8(q, k, v, signs=sd, causal=w.causal, scale=w.scale,
+                                        block_mask=mask, out=o, lse=lse, workspace=ws))
+    prep = timed(lambda: fa.fp8_prepare(q, k, v, sd, workspace=ws))
+    mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
+    f_fwd, _ = flops(w, mask.cpu() if mask is not None else None)
+    tf = f_fwd / (mean(call) * 1e-3) / 1e12
+    rec = recorded_traffic(w.name)
+    out = {"workload": w.name, "rotation": "random Hadamard (seeded signs)",
+           "ms": round(mean(call), 4),
+           "ms_median_min": [round(statistics.median(call), 4), round(min(call), 4)],
+           "prep_ms": round(mean(prep), 4), "tflops": round(tf, 2),
+           "vs_bf16_forward": None,
+           "roofline": {"bound": "mfma", "kernel": "fa_forward_fp8 (fp8_prep + fwd8)",
+                        "achieved": round(tf, 2), "peak": PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",
+                        "frac": round(tf / PEAK_TFLOPS["fp8"], 4),
+                        "traffic": None if rec is None else rec["bytes_per_call"].get("fp8"),
+                        "avg_ms": round(mean(call), 4)}}
+    if with_cpu:
+        out["cpu_baseline"] = fp8_cpu_baseline(w, inputs, signs, cpu_heads)
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -329,6 +409,10 @@ def main():
             "bwd": round(mean(d_bwd) / mean(bwd_ms) * kept, 4) if w.backward else None,
             "dense_fwd_ms": round(mean(d_fwd), 4),
             "dense_bwd_ms": round(mean(d_bwd), 4) if w.backward else None}
+    if not args.no_fp8 and w.dtype in ("bf16", "f16"):
+        out["fp8"] = bench_fp8(fa, w, inputs, tensors, mask, args.steps, args.warmup,
+                               args.fp8_cpu_heads, not args.no_cpu_baseline)
+        out["fp8"]["vs_bf16_forward"] = round(mean(fwd_ms) / out["fp8"]["ms"], 3)
     if not args.no_decode:
         out["decode"] = bench_decode(fa, args.decode_workload, args.steps, args.warmup,
                                      args.decode_cpu_heads, not args.no_cpu_baseline)
