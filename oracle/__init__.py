@@ -23,6 +23,11 @@ Pages cited in this package (the reader has these pages):
   изменило на практике" (decoding: a few queries against a long history).
 * marketmaker.cc page, section "FA3 : Mécanique de la trémie", point 3 (FP8
   with incoherent processing: random rotation, then per-block quantisation).
+* Dropout fused into the kernel: the reading guide's "Ideias centrais"
+  ("Fusão de Kernels") and the marketmaker.cc page's `dropout_p` argument
+  ("L'intégration est de huit lignes"); the mask comes from Philox-4x32-10
+  (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3",
+  SC 2011).
 
 Every function in this package has at least one pin in
 ``tests/test_oracle_*.py`` that checks it against something other than
@@ -46,6 +51,14 @@ from .decode import (  # noqa: F401
     decode_allowed,
     decode_head,
     split_partials,
+)
+from .dropout import (  # noqa: F401
+    backward_head_dropout,
+    forward_head_dropout,
+    keep_mask,
+    keep_scale,
+    keep_threshold,
+    philox,
 )
 from .fp8 import (  # noqa: F401
     E4M3_MAX,
