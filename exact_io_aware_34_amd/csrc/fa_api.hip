@@ -72,6 +72,28 @@ int check_decode(int B, int H, int Nq, int Nk, int d, float scale, int dtype, in
   return FA_OK;
 }
 
+// Dropout: byte threshold t = round(256 p) (clamped to 255) and the scale
+// 1 / (1 - t / 256) of the kept values.  Returns false for p outside [0, 1).
+bool dropout_args(float p, uint64_t seed, uint32_t offset, uint32_t& k0, uint32_t& k1,
+                  uint32_t& off, uint32_t& t8, float& scale) {
+  if (!std::isfinite(p) || p < 0.f || p >= 1.f) return false;
+  t8 = (uint32_t)std::min(255.0, std::floor((double)p * 256.0 + 0.5));
+  scale = (float)(256.0 / (256.0 - (double)t8));
+  k0 = (uint32_t)(seed & 0xFFFFFFFFu);
+  k1 = (uint32_t)(seed >> 32);
+  off = offset;
+  return true;
+}
+
+int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int N, int d, float scale, int causal, const uint8_t* block_mask, int dtype,
+                 float dropout_p, uint64_t seed, uint32_t offset, void* stream);
+int backward_impl(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                  const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, int d,
+                  float scale, int causal, const uint8_t* block_mask, int dtype, float dropout_p,
+                  uint64_t seed, uint32_t offset, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
 // FP8 workspace regions, in order, each padded to 256 bytes.
 struct Fp8Layout {
   size_t q8, k8, v8t, sq, sk, sv, total;
@@ -142,6 +164,25 @@ const char* fa_status_string(int status) {
 int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int N, int d, float scale, int causal,
                const uint8_t* block_mask, int dtype, void* stream) {
+  return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, dtype, 0.f, 0, 0,
+                      stream);
+}
+
+int fa_forward_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int N, int d, float scale, int causal,
+                       const uint8_t* block_mask, int dtype, float dropout_p, uint64_t seed,
+                       uint32_t offset, void* stream) {
+  return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, dtype, dropout_p,
+                      seed, offset, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int N, int d, float scale, int causal, const uint8_t* block_mask, int dtype,
+                 float dropout_p, uint64_t seed, uint32_t offset, void* stream) {
   if (!tensor_ptr_ok(q) || !tensor_ptr_ok(k) || !tensor_ptr_ok(v) || !tensor_ptr_ok(o))
     return FA_ERR_INVALID_ARG;
   if (lse == nullptr || !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
@@ -162,9 +203,17 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
   p.scale = scale;
   p.scale_log2e = scale * kLog2e;
   p.rescale_thr = 8.0f / p.scale_log2e;  // 2^8 headroom for the exponentials
+  if (!dropout_args(dropout_p, seed, offset, p.drop_k0, p.drop_k1, p.drop_off, p.drop_t8,
+                    p.drop_scale))
+    return FA_ERR_INVALID_ARG;
+  if (p.drop_t8 > 0 && dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   const hipError_t e = fa::launch_forward(p, dtype, d, causal != 0, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
+
+}  // namespace
+
+extern "C" {
 
 size_t fa_backward_workspace_size(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
@@ -177,6 +226,44 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
                 int B, int H, int N, int d, float scale, int causal,
                 const uint8_t* block_mask, int dtype,
                 void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, block_mask,
+                       dtype, 0.f, 0, 0, workspace, workspace_bytes, stream);
+}
+
+int fa_backward_dropout(const void* q, const void* k, const void* v, const void* o,
+                        const void* dO, const float* lse, float* dq, float* dk, float* dv,
+                        int B, int H, int N, int d, float scale, int causal,
+                        const uint8_t* block_mask, int dtype, float dropout_p, uint64_t seed,
+                        uint32_t offset, void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, block_mask,
+                       dtype, dropout_p, seed, offset, workspace, workspace_bytes, stream);
+}
+
+int fa_dropout_mask(int B, int H, int N, float dropout_p, uint64_t seed, uint32_t offset,
+                    uint8_t* keep, void* stream) {
+  if (keep == nullptr || B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARG;
+  if ((long long)B * H > (1LL << 24) || N > 65536) return FA_ERR_UNSUPPORTED;
+  const long long nq = (N + 3) / 4;
+  if ((long long)B * H * nq * nq > (1LL << 31) * 255LL) return FA_ERR_UNSUPPORTED;  // grid size
+  fa::DropMaskParams p{};
+  float sc;
+  if (!dropout_args(dropout_p, seed, offset, p.k0, p.k1, p.off, p.t8, sc)) return FA_ERR_INVALID_ARG;
+  p.keep = keep;
+  p.BH = B * H;
+  p.N = N;
+  const hipError_t e = fa::launch_dropout_mask(p, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"
+
+namespace {
+
+int backward_impl(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                  const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, int d,
+                  float scale, int causal, const uint8_t* block_mask, int dtype, float dropout_p,
+                  uint64_t seed, uint32_t offset, void* workspace, size_t workspace_bytes,
+                  void* stream) {
   if (!tensor_ptr_ok(q) || !tensor_ptr_ok(k) || !tensor_ptr_ok(v) || !tensor_ptr_ok(o) ||
       !tensor_ptr_ok(dO) || !tensor_ptr_ok(dq) || !tensor_ptr_ok(dk) || !tensor_ptr_ok(dv))
     return FA_ERR_INVALID_ARG;
@@ -205,9 +292,16 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
   p.mask_tiles = (N + fa::MASK_TILE - 1) / fa::MASK_TILE;
   p.scale = scale;
   p.scale_log2e = scale * kLog2e;
+  if (!dropout_args(dropout_p, seed, offset, p.drop_k0, p.drop_k1, p.drop_off, p.drop_t8,
+                    p.drop_scale))
+    return FA_ERR_INVALID_ARG;
   const hipError_t e = fa::launch_backward(p, dtype, d, causal != 0, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
+
+}  // namespace
+
+extern "C" {
 
 size_t fa_forward_fp8_workspace_size(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return 0;

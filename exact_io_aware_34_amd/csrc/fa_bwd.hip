@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, c
 // (K, V rows as MFMA operands in VGPRs, dK and dV accumulators) and streams
 // 64-row Q / dO tiles plus their statistics through a 4-slot LDS ring, copies
 // issued two tiles ahead.
-template <typename T, int D, bool CAUSAL, bool SPARSE>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdParams p) {
   using VT = typename V8<T>::t;
   constexpr int NW = 4, BC = NW * 32, QT = 64, NS = 4;
@@ -157,14 +157,14 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdPara
 
   const int i_end = (N + QT - 1) / QT;
   const int i_beg = CAUSAL ? k0 / QT : 0;
-  auto next_active = [&](int i) {
+  auto next_active = [&](int i) __attribute__((always_inline)) {
     if (SPARSE)
       while (i < i_end && mask_s[(i * QT) / MASK_TILE] == 0) ++i;
     return i;
   };
   // Copy query tile i (Q, dO, statistics) into slot `slot`.  Rows past N read
   // row N - 1; their scores are masked, so they contribute nothing.
-  auto issue = [&](int i, int slot) {
+  auto issue = [&](int i, int slot) __attribute__((always_inline)) {
     const int qa = i * QT;
     const uint32_t qd = lds0 + (uint32_t)(slot * STAGE * (int)sizeof(T));
     const uint32_t od = qd + (uint32_t)(TILE * (int)sizeof(T));
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdPara
 
   // S = Q K^T and dP = dO V^T of half h of the tile in slot SL: lane = key,
   // register r = query 32h + 8(r/4) + 4g + r%4 of the tile.
-  auto sdp = [&](int slot, int h, f32x16& s, f32x16& dp) {
+  auto sdp = [&](int slot, int h, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
     const T* qt_ = lds + slot * STAGE + 32 * h * D;
     s = f32x16{};
     dp = f32x16{};
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdPara
     }
   };
   // dV += P^T dO and dK += dS^T Q for half h of the tile in slot SL.
-  auto grads = [&](int slot, int h, const VT (&pa)[2], const VT (&dsa)[2]) {
+  auto grads = [&](int slot, int h, const VT (&pa)[2], const VT (&dsa)[2]) __attribute__((always_inline)) {
     const T* qt_ = lds + slot * STAGE + 32 * h * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -241,8 +241,15 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdPara
       }
   };
   // P and dS of half h of the tile in slot SL, rounded to 16-bit operands.
-  auto pds = [&](int slot, int h, const f32x16& s, const f32x16& dp, VT (&pa)[2], VT (&dsa)[2]) {
+  // With dropout (queries qb + 8t + 4g + e of the unit, this lane's key):
+  // P^T for dV keeps only the kept probabilities (1 / (1 - p) is applied to
+  // dV at the end) and dS = P o (Z dP / (1 - p) - D).
+  auto pds = [&](int slot, int h, int qb, const f32x16& s, const f32x16& dp, VT (&pa)[2],
+                 VT (&dsa)[2]) __attribute__((always_inline)) {
     const float* sf = &st_s[slot][32 * h];
+    uint32_t dwk[4];
+    if constexpr (DROP)
+      drop_words_key_lane(dwk, qb, kw0, l32, g, (uint32_t)bh, p.drop_off, p.drop_k0, p.drop_k1);
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
       const float4 l4 = *(const float4*)(sf + 8 * rg + 4 * g);
@@ -253,7 +260,13 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdPara
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         pv[e] = fast_exp2(fmaf(s[4 * rg + e], c, -lv[e]));
-        dsv[e] = pv[e] * (dp[4 * rg + e] - dd[e]);
+        if constexpr (DROP) {
+          const bool kp = drop_keep(dwk, 4 * rg + e, p.drop_t8);
+          dsv[e] = pv[e] * ((kp ? dp[4 * rg + e] * p.drop_scale : 0.f) - dd[e]);
+          pv[e] = kp ? pv[e] : 0.f;
+        } else {
+          dsv[e] = pv[e] * (dp[4 * rg + e] - dd[e]);
+        }
       }
       const int kk = rg >> 1, w0 = 2 * (rg & 1);
       u32x4 pw = __builtin_bit_cast(u32x4, pa[kk]);
@@ -268,7 +281,7 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdPara
   };
   // Query q sees key my_k iff q >= my_k (causal) and q < N; S = -inf
   // elsewhere.  Units entirely before this wave's keys are masked whole.
-  auto mask_unit = [&](int qa, f32x16& s) {
+  auto mask_unit = [&](int qa, f32x16& s) __attribute__((always_inline)) {
     if ((CAUSAL && qa <= kw0) || qa + 32 > N) {
       const int first = CAUSAL ? my_k : 0;  // first visible query
 #pragma unroll
@@ -281,11 +294,11 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdPara
   // One block: the gradient products of unit u-1 beside the element-wise
   // work of unit u, then S and dP of unit u+1 (issued last, so the scores of
   // units u and u+1 are not both live while the vector work runs).
-  auto block = [&](int rslc, int gslc, int eslc, int h, int he, f32x16& s_cur, f32x16& dp_cur,
-                   f32x16& s_nxt, f32x16& dp_nxt, const VT (&pa_p)[2], const VT (&ds_p)[2],
-                   VT (&pa_c)[2], VT (&ds_c)[2]) {
+  auto block = [&](int rslc, int gslc, int eslc, int h, int he, int qb, f32x16& s_cur,
+                   f32x16& dp_cur, f32x16& s_nxt, f32x16& dp_nxt, const VT (&pa_p)[2],
+                   const VT (&ds_p)[2], VT (&pa_c)[2], VT (&ds_c)[2]) __attribute__((always_inline)) {
     grads(gslc, h, pa_p, ds_p);
-    pds(eslc, he, s_cur, dp_cur, pa_c, ds_c);
+    pds(eslc, he, qb, s_cur, dp_cur, pa_c, ds_c);
     sdp(rslc, h, s_nxt, dp_nxt);
     keep_here(pa_c);
     keep_here(ds_c);
@@ -307,14 +320,14 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdPara
     sdp(0, 0, s_even, dp_even);
     mask_unit(iq[0] * QT, s_even);
     sdp(0, 1, s_odd, dp_odd);
-    pds(0, 0, s_even, dp_even, pa_even, ds_even);
+    pds(0, 0, iq[0] * QT, s_even, dp_even, pa_even, ds_even);
   }
   // One iteration; the slot is a run-time index (four unrolled copies with
   // constant slots need more registers than the occupancy allows).  MASKED
   // iterations apply the edge masks; the others are branch-free between
   // their two blocks.
   int n = 0;
-  auto iteration = [&](auto masked_c) {
+  auto iteration = [&](auto masked_c) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_c)::value;
     const int SL = n & (NS - 1), SL1 = (n + 1) & (NS - 1);  // slots of tiles n, n+1
     const int i = iq[0], i1 = iq[1];
@@ -326,9 +339,11 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdPara
     // Units 2n+1 (second half of tile n) and 2n+2 (first half of tile n+1;
     // past the last tile it is masked whole and never used).
     if constexpr (MASKED) mask_unit(i * QT + 32, s_odd);
-    block(SL1, SL, SL, 0, 1, s_odd, dp_odd, s_even, dp_even, pa_even, ds_even, pa_odd, ds_odd);
+    block(SL1, SL, SL, 0, 1, i * QT + 32, s_odd, dp_odd, s_even, dp_even, pa_even, ds_even, pa_odd,
+          ds_odd);
     if constexpr (MASKED) mask_unit(i1 < i_end ? i1 * QT : N, s_even);
-    block(SL1, SL, SL1, 1, 0, s_even, dp_even, s_odd, dp_odd, pa_odd, ds_odd, pa_even, ds_even);
+    block(SL1, SL, SL1, 1, 0, i1 * QT, s_even, dp_even, s_odd, dp_odd, pa_odd, ds_odd, pa_even,
+          ds_even);
 #pragma unroll
     for (int t = 0; t < NS - 1; ++t) iq[t] = iq[t + 1];
     iq[NS - 1] = iq[NS - 2] < i_end ? next_active(iq[NS - 2] + 1) : i_end;
@@ -337,7 +352,7 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdPara
   // Iterations needing no mask (units 2n+1, 2n+2 past the causal diagonal
   // and inside N) form one contiguous run: masked ones come before it
   // (causal diagonal) and after it (row tail).
-  auto interior = [&]() {
+  auto interior = [&]() __attribute__((always_inline)) {
     return (!CAUSAL || iq[0] * QT + 32 > kw0) && iq[1] < i_end && iq[1] * QT + 32 <= N;
   };
   while (iq[0] < i_end && !interior()) iteration(std::true_type{});
@@ -354,7 +369,7 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdPara
       const int key = kw0 + 8 * (r >> 2) + 4 * g + (r & 3);
       if (key < N) {
         dK[(size_t)key * D + 32 * db + l32] = dk[db][r] * p.scale;
-        dV[(size_t)key * D + 32 * db + l32] = dv[db][r];
+        dV[(size_t)key * D + 32 * db + l32] = DROP ? dv[db][r] * p.drop_scale : dv[db][r];
       }
     }
 }
@@ -364,7 +379,7 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdPara
 // slots, V: 3), copies issued two tiles ahead.  S^T = K Q^T and
 // dP^T = V dO^T take Q and dO from VGPRs; dQ^T += K^T dS^T reads K
 // transposed.
-template <typename T, int D, bool CAUSAL, bool SPARSE>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dq_u_kernel(BwdParams p) {
   using VT = typename V8<T>::t;
   constexpr int NW = 4, BR = NW * 32, BC = 64, NK = 4, NV = 3;
@@ -426,7 +441,7 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dq_u_kernel(BwdParams
   const int n_kt = (N + BC - 1) / BC;
   int kt_end = n_kt;
   if (CAUSAL) kt_end = min(kt_end, (min(N, (qt + 1) * BR) + BC - 1) / BC);
-  auto next_active = [&](int jj) {
+  auto next_active = [&](int jj) __attribute__((always_inline)) {
     if (SPARSE)
       while (jj < kt_end && mask_s[(jj * BC) / MASK_TILE] == 0) ++jj;
     return jj;
@@ -436,7 +451,7 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dq_u_kernel(BwdParams
 
   // Copy tile jj of K (or V) into slot `slot` of its ring.  Rows past N read
   // row N - 1; their scores are masked, so they contribute nothing.
-  auto issue = [&](const T* src, int jj, uint32_t dst_slot) {
+  auto issue = [&](const T* src, int jj, uint32_t dst_slot) __attribute__((always_inline)) {
     const int k0 = jj * BC;
     const uint32_t dst = lds0 + dst_slot * (uint32_t)(TILE * (int)sizeof(T));
     if (k0 + BC <= N) {
@@ -481,7 +496,7 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dq_u_kernel(BwdParams
 
   // S^T = K Q^T and dP^T = V dO^T of half h of K slot KS / V slot VS: lane =
   // query, register r = key 32h + 8(r/4) + 4g + r%4 of the tile.
-  auto sdp = [&](int kslot, int vslot, int h, f32x16& s, f32x16& dp) {
+  auto sdp = [&](int kslot, int vslot, int h, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
     const T* kt = kvs + kslot * TILE + 32 * h * D;
     const T* vt = kvs + (NK + vslot) * TILE + 32 * h * D;
     s = f32x16{};
@@ -493,7 +508,7 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dq_u_kernel(BwdParams
     }
   };
   // dQ^T += K^T dS^T for half h of K slot KS (K read transposed).
-  auto dqacc = [&](int kslot, int h, const VT (&dsf)[2]) {
+  auto dqacc = [&](int kslot, int h, const VT (&dsf)[2]) __attribute__((always_inline)) {
     const T* kt = kvs + kslot * TILE + 32 * h * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -505,7 +520,11 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dq_u_kernel(BwdParams
       }
   };
   // dS^T = P^T o (dP^T - D) with P = exp2(S c - lse2), rounded to 16 bits.
-  auto dscores = [&](const f32x16& s, const f32x16& dp, VT (&dsf)[2]) {
+  // With dropout (keys ks + 8t + 4g + e of the unit): dS = P o (Z dP / (1 - p) - D).
+  auto dscores = [&](int ks, const f32x16& s, const f32x16& dp, VT (&dsf)[2]) __attribute__((always_inline)) {
+    uint32_t dwq[4];
+    if constexpr (DROP)
+      drop_words_query_lane(dwq, ks, q0, l32, g, (uint32_t)bh, p.drop_off, p.drop_k0, p.drop_k1);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       u32x4 w;
@@ -514,14 +533,19 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dq_u_kernel(BwdParams
         const int r = 8 * h + 2 * e;
         const float p0 = fast_exp2(fmaf(s[r], c, -lq));
         const float p1 = fast_exp2(fmaf(s[r + 1], c, -lq));
-        w[e] = pack2<T>(p0 * (dp[r] - dq_row), p1 * (dp[r + 1] - dq_row));
+        float d0 = dp[r], d1 = dp[r + 1];
+        if constexpr (DROP) {
+          d0 = drop_keep(dwq, r, p.drop_t8) ? d0 * p.drop_scale : 0.f;
+          d1 = drop_keep(dwq, r + 1, p.drop_t8) ? d1 * p.drop_scale : 0.f;
+        }
+        w[e] = pack2<T>(p0 * (d0 - dq_row), p1 * (d1 - dq_row));
       }
       dsf[h] = __builtin_bit_cast(VT, w);
     }
   };
   // Keys past this lane's last visible key (causal diagonal, keys >= N)
   // become -inf; a unit past the wave's range is masked whole.
-  auto mask_unit = [&](int ks, f32x16& s) {
+  auto mask_unit = [&](int ks, f32x16& s) __attribute__((always_inline)) {
     if ((CAUSAL && ks + 31 > q0) || ks + 32 > N) {
       const int lim = min(N - 1, CAUSAL ? my_q : N - 1) - ks - 4 * g;
 #pragma unroll
@@ -529,12 +553,12 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dq_u_kernel(BwdParams
         if (8 * (r >> 2) + (r & 3) > lim) s[r] = -INFINITY;
     }
   };
-  auto block = [&](int kslc, int vslc, int gslc, int h, f32x16& s_cur, f32x16& dp_cur,
-                   f32x16& s_nxt, f32x16& dp_nxt, const VT (&ds_p)[2], VT (&ds_c)[2]) {
+  auto block = [&](int kslc, int vslc, int gslc, int h, int ks, f32x16& s_cur, f32x16& dp_cur,
+                   f32x16& s_nxt, f32x16& dp_nxt, const VT (&ds_p)[2], VT (&ds_c)[2]) __attribute__((always_inline)) {
     sdp(kslc, vslc, h, s_nxt, dp_nxt);
     dqacc(gslc, h, ds_p);
-    dscores(s_cur, dp_cur, ds_c);
-    if constexpr (D == 64) sched_interleave<12, 8, 1, 6>();
+    dscores(ks, s_cur, dp_cur, ds_c);
+    if constexpr (D == 64 && !DROP) sched_interleave<12, 8, 1, 6>();
     keep_here(ds_c);
   };
 
@@ -555,13 +579,13 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dq_u_kernel(BwdParams
     sdp(0, 0, 0, s_even, dp_even);
     mask_unit(jq[0] * BC, s_even);
     sdp(0, 0, 1, s_odd, dp_odd);
-    dscores(s_even, dp_even, ds_even);
+    dscores(jq[0] * BC, s_even, dp_even, ds_even);
   }
   // One iteration; the slots are run-time indices (K: n mod 4, V: n mod 3).
   // MASKED iterations apply the edge masks; the others are branch-free
   // between their two blocks.
   int n = 0, vs0 = 0;  // vs0: V slot of tile n
-  auto iteration = [&](auto masked_c) {
+  auto iteration = [&](auto masked_c) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_c)::value;
     const int KS0 = n & (NK - 1), KS1 = (n + 1) & (NK - 1);
     const int VS1 = vs0 == NV - 1 ? 0 : vs0 + 1;
@@ -576,9 +600,9 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dq_u_kernel(BwdParams
     }
     if (!MASKED || jj * BC <= last_key) {
       if constexpr (MASKED) mask_unit(jj * BC + 32, s_odd);
-      block(KS1, VS1, KS0, 0, s_odd, dp_odd, s_even, dp_even, ds_even, ds_odd);
+      block(KS1, VS1, KS0, 0, jj * BC + 32, s_odd, dp_odd, s_even, dp_even, ds_even, ds_odd);
       if constexpr (MASKED) mask_unit(j1 < kt_end ? j1 * BC : N, s_even);
-      block(KS1, VS1, KS0, 1, s_even, dp_even, s_odd, dp_odd, ds_odd, ds_even);
+      block(KS1, VS1, KS0, 1, j1 * BC, s_even, dp_even, s_odd, dp_odd, ds_odd, ds_even);
     }
     vs0 = VS1;
 #pragma unroll
@@ -605,7 +629,7 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dq_u_kernel(BwdParams
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool SPARSE>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
   const size_t rows = (size_t)p.BH * p.N;
   const size_t threads = rows * (D / 8);
@@ -614,19 +638,25 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid(((p.N + 127) / 128) * p.BH), block(256);
-  bwd_dkdv_u_kernel<T, D, CAUSAL, SPARSE><<<grid, block, 0, st>>>(p);
+  bwd_dkdv_u_kernel<T, D, CAUSAL, SPARSE, DROP><<<grid, block, 0, st>>>(p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  bwd_dq_u_kernel<T, D, CAUSAL, SPARSE><<<grid, block, 0, st>>>(p);
+  bwd_dq_u_kernel<T, D, CAUSAL, SPARSE, DROP><<<grid, block, 0, st>>>(p);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_bwd(const BwdParams& p, bool causal, bool sparse, hipStream_t st) {
-  if (causal && sparse) return launch_bwd_t<T, D, true, true>(p, st);
-  if (causal) return launch_bwd_t<T, D, true, false>(p, st);
-  if (sparse) return launch_bwd_t<T, D, false, true>(p, st);
-  return launch_bwd_t<T, D, false, false>(p, st);
+  if (p.drop_t8 > 0) {
+    if (causal && sparse) return launch_bwd_t<T, D, true, true, true>(p, st);
+    if (causal) return launch_bwd_t<T, D, true, false, true>(p, st);
+    if (sparse) return launch_bwd_t<T, D, false, true, true>(p, st);
+    return launch_bwd_t<T, D, false, false, true>(p, st);
+  }
+  if (causal && sparse) return launch_bwd_t<T, D, true, true, false>(p, st);
+  if (causal) return launch_bwd_t<T, D, true, false, false>(p, st);
+  if (sparse) return launch_bwd_t<T, D, false, true, false>(p, st);
+  return launch_bwd_t<T, D, false, false, false>(p, st);
 }
 
 }  // namespace

@@ -227,6 +227,110 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---- Dropout mask: Philox-4x32-10 over 4 x 4 (query, key) blocks ----
+//
+// Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011): ten rounds of
+//   (x0, x1, x2, x3) <- (hi(M1 x2) ^ x1 ^ k0, lo(M1 x2), hi(M0 x0) ^ x3 ^ k1, lo(M0 x0))
+// with the key advanced by the Weyl constants between rounds.  Element
+// (query i, key j) of head bh uses byte j % 4 of word i % 4 of the output at
+// counter (j / 4, i / 4, bh, offset), key (seed_lo, seed_hi); it is kept iff
+// that byte is >= the threshold t = round(256 p).
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                              uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+  }
+  return u32x4{c0, c1, c2, c3};
+}
+
+__device__ __forceinline__ uint32_t quad_swap1(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true);  // lanes l ^ 1
+}
+__device__ __forceinline__ uint32_t quad_swap2(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, true);  // lanes l ^ 2
+}
+
+// Transpose across the four lanes of a quad: lane w ends with r[t] = the
+// r[w] that quad lane t held (two exchange stages, lane bits 0 and 1).
+__device__ __forceinline__ void quad_transpose4(uint32_t (&r)[4], int w) {
+#pragma unroll
+  for (int b = 1; b <= 2; b <<= 1) {
+    const bool hi = (w & b) != 0;
+#pragma unroll
+    for (int j0 = 0; j0 < 4; ++j0) {
+      if (j0 & b) continue;
+      const int j1 = j0 | b;
+      // Value selects with unconditional stores keep r in registers.
+      const uint32_t a = r[j0], c = r[j1];
+      const uint32_t send = hi ? a : c;
+      const uint32_t recv = b == 1 ? quad_swap1(send) : quad_swap2(send);
+      r[j0] = hi ? recv : a;
+      r[j1] = hi ? c : recv;
+    }
+  }
+}
+
+// In-lane transpose of the 4 x 4 byte matrix held in r (word w, byte b ->
+// word b, byte w).
+__device__ __forceinline__ void byte_transpose4(uint32_t (&r)[4]) {
+  uint32_t o[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    o[b] = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) o[b] |= ((r[w] >> (8 * b)) & 0xFFu) << (8 * w);
+  }
+#pragma unroll
+  for (int b = 0; b < 4; ++b) r[b] = o[b];
+}
+
+// Keep bytes for a lane that holds one query and the 16 keys
+// ks + 8 t + 4 g + e (t, e = 0..3) of a 32-key unit (the S^T layout):
+// word t, byte e.  Each lane of a quad computes one Philox call (the 4 x 4
+// block of its quad's queries and key group t = its quad index) and the quad
+// exchanges words.
+__device__ __forceinline__ void drop_words_query_lane(uint32_t (&c)[4], int ks, int q0, int l32,
+                                                      int g, uint32_t bh, uint32_t off,
+                                                      uint32_t k0, uint32_t k1) {
+  const int w = l32 & 3;
+  const u32x4 r = philox4x32_10((uint32_t)(ks / 4 + 2 * w + g), (uint32_t)((q0 + l32) / 4), bh,
+                                off, k0, k1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = r[i];
+  quad_transpose4(c, w);
+}
+
+// Keep bytes for a lane that holds one key and the 16 queries
+// qb + 8 t + 4 g + e of a 32-query unit (the S layout): word t, byte e.
+__device__ __forceinline__ void drop_words_key_lane(uint32_t (&c)[4], int qb, int k0w, int l32,
+                                                    int g, uint32_t bh, uint32_t off,
+                                                    uint32_t k0, uint32_t k1) {
+  const int w = l32 & 3;
+  const u32x4 r = philox4x32_10((uint32_t)((k0w + l32) / 4), (uint32_t)(qb / 4 + 2 * w + g), bh,
+                                off, k0, k1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = r[i];
+  byte_transpose4(c);
+  quad_transpose4(c, w);
+}
+
+__device__ __forceinline__ bool drop_keep(const uint32_t (&c)[4], int r, uint32_t t8) {
+  return ((c[r >> 2] >> (8 * (r & 3))) & 0xFFu) >= t8;
+}
+
 // Workgroup index -> logical tile index.  The hardware hands consecutive
 // workgroup ids to the 8 XCDs round robin; this mapping gives each XCD a
 // contiguous range of logical ids so tiles of one head share that XCD's L2.

@@ -40,7 +40,7 @@ namespace {
 template <int V>
 using ic = std::integral_constant<int, V>;
 
-template <typename T, int D, bool CAUSAL, bool SPARSE>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p) {
   using VT = typename V8<T>::t;
   using HT = typename V8<T>::h;
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p)
   const int n_kt = (N + BC - 1) / BC;
   int kt_end = n_kt;
   if (CAUSAL) kt_end = min(kt_end, (min(N, (qt + 1) * BR) + BC - 1) / BC);
-  auto next_active = [&](int jj) {
+  auto next_active = [&](int jj) __attribute__((always_inline)) {
     if (SPARSE)
       while (jj < kt_end && mask_s[(jj * BC) / MASK_TILE] == 0) ++jj;
     return jj;
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p)
   // Copy tile jj of K (or V) into slot `slot` of its ring.  Rows past N read
   // row N - 1: those keys are masked out of every score that is used, and
   // their values meet probability 0.
-  auto issue = [&](const T* src, int jj, int slot, bool is_v) {
+  auto issue = [&](const T* src, int jj, int slot, bool is_v) __attribute__((always_inline)) {
     const int k0 = jj * BC;
     const uint32_t dst = lds0 + (uint32_t)(((is_v ? NS : 0) + slot) * TILE * (int)sizeof(T));
     if (k0 + BC <= N) {
@@ -176,14 +176,14 @@ __global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p)
 
   // ---- work on one 32-key unit ----
   // S^T[key][query] of half h of the K tile in slot SL.
-  auto s_unit = [&](auto slc, int h, f32x16& s) {
+  auto s_unit = [&](auto slc, int h, f32x16& s) __attribute__((always_inline)) {
     const T* kt = kvs + decltype(slc)::value * TILE + 32 * h * D;
     s = f32x16{};
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) s = mfma32x32x16(*(const VT*)(kt + koff[ds]), qf[ds], s);
   };
   // O^T += V^T P^T for half h of the V tile in slot SL (two 16-key steps).
-  auto pv_unit = [&](auto slc, int h, const VT (&pu)[2]) {
+  auto pv_unit = [&](auto slc, int h, const VT (&pu)[2]) __attribute__((always_inline)) {
     const T* vt = kvs + (NS + decltype(slc)::value) * TILE + 32 * h * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -196,7 +196,9 @@ __global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p)
   };
   // Exponentials of one unit's scores against the current reference; returns
   // the lane's fp32 sum and writes the two 16-bit P^T operands.
-  auto exps = [&](const f32x16& s, VT (&pu)[2]) {
+  // With dropout the row sum takes every exponential and the P V operand
+  // only the kept ones (the 1 / (1 - p) scale is applied at the end).
+  auto exps = [&](const f32x16& s, VT (&pu)[2], const uint32_t (&dw)[4]) __attribute__((always_inline)) {
     const float mc = m_run * c;
     float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
@@ -205,10 +207,14 @@ __global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 8 * h + 2 * e;
-        const float e0 = fast_exp2(fmaf(s[r], c, -mc));
-        const float e1 = fast_exp2(fmaf(s[r + 1], c, -mc));
+        float e0 = fast_exp2(fmaf(s[r], c, -mc));
+        float e1 = fast_exp2(fmaf(s[r + 1], c, -mc));
         ls0 += e0;
         ls1 += e1;
+        if constexpr (DROP) {
+          e0 = drop_keep(dw, r, p.drop_t8) ? e0 : 0.f;
+          e1 = drop_keep(dw, r + 1, p.drop_t8) ? e1 : 0.f;
+        }
         w[e] = pack2<T>(e0, e1);
       }
       pu[h] = __builtin_bit_cast(VT, w);
@@ -222,7 +228,7 @@ __global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p)
   // exponentials are recomputed.  O, l and lse share the reference, so the
   // result does not depend on it.  O already holds every earlier unit
   // (including the one whose P V was issued in the same block).
-  auto settle = [&](float ls, const f32x16& s, VT (&pu)[2]) {
+  auto settle = [&](float ls, const f32x16& s, VT (&pu)[2], const uint32_t (&dw)[4]) __attribute__((always_inline)) {
     if (wave_any(!(ls <= 256.f))) {
       float mx = s[0];
 #pragma unroll
@@ -233,14 +239,14 @@ __global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p)
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
-      ls = exps(s, pu);
+      ls = exps(s, pu, dw);
     }
     l_run += ls;
   };
   // Scores of keys past this lane's last visible key (causal diagonal, keys
   // >= N) become -inf.  A unit past the wave's range is masked entirely, so
   // its probabilities are exactly 0 and its P V adds nothing.
-  auto mask_unit = [&](int ks, f32x16& s) {
+  auto mask_unit = [&](int ks, f32x16& s) __attribute__((always_inline)) {
     if (ks + 31 > plain_key) {
       const int lim = min(N - 1, CAUSAL ? q0w + l32 : N - 1) - ks - 4 * g;
 #pragma unroll
@@ -251,14 +257,25 @@ __global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p)
   // One block: matrix work of the neighbouring units (scores of the next,
   // P V of the previous) beside the exponentials of this one, with every LDS
   // read issued first.
-  auto block = [&](auto kslc, auto vslc, int h, f32x16& s_cur, f32x16& s_nxt,
-                   const VT (&p_prv)[2], VT (&p_cur)[2]) {
+  // Keep bytes of the unit starting at key ks (dropout only).
+  auto drop_words = [&](int ks, uint32_t (&dw)[4]) __attribute__((always_inline)) {
+    if constexpr (DROP)
+      drop_words_query_lane(dw, ks, q0w, l32, g, (uint32_t)bh, p.drop_off, p.drop_k0, p.drop_k1);
+  };
+  auto block = [&](auto kslc, auto vslc, int h, int ks_cur, f32x16& s_cur, f32x16& s_nxt,
+                   const VT (&p_prv)[2], VT (&p_cur)[2]) __attribute__((always_inline)) {
     s_unit(kslc, h, s_nxt);
     pv_unit(vslc, h, p_prv);
-    const float ls = exps(s_cur, p_cur);
-    if constexpr (D == 64) sched_interleave<8, 12, 0, 7>();
-    else sched_interleave<16, 12, 1, 4>();
-    settle(ls, s_cur, p_cur);
+    uint32_t dw[4];
+    drop_words(ks_cur, dw);
+    const float ls = exps(s_cur, p_cur, dw);
+    if constexpr (DROP) {
+    } else if constexpr (D == 64) {
+      sched_interleave<8, 12, 0, 7>();
+    } else {
+      sched_interleave<16, 12, 1, 4>();
+    }
+    settle(ls, s_cur, p_cur, dw);
   };
 
   // Units are numbered along the active tiles, two per tile.  Block u
@@ -285,9 +302,11 @@ __global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p)
     s_unit(ic<0>{}, 0, s_even);
     mask_unit(jq[0] * BC, s_even);
     s_unit(ic<0>{}, 1, s_odd);
-    settle(exps(s_even, p_even), s_even, p_even);
+    uint32_t dw[4];
+    drop_words(jq[0] * BC, dw);
+    settle(exps(s_even, p_even, dw), s_even, p_even, dw);
   }
-  auto iter = [&](auto slc) {
+  auto iter = [&](auto slc) __attribute__((always_inline)) {
     constexpr int SL = decltype(slc)::value;        // n % NS
     constexpr int SL1 = (SL + 1) % NS;              // slot of tile n+1
     const int j = jq[0], j1 = jq[1];
@@ -303,9 +322,9 @@ __global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p)
     // past the last tile, which masks unit 2n+2 entirely).
     if (j * BC <= last_key) {
       mask_unit(j * BC + 32, s_odd);
-      block(ic<SL1>{}, ic<SL>{}, 0, s_odd, s_even, p_even, p_odd);
+      block(ic<SL1>{}, ic<SL>{}, 0, j * BC + 32, s_odd, s_even, p_even, p_odd);
       mask_unit(j1 * BC, s_even);
-      block(ic<SL1>{}, ic<SL>{}, 1, s_even, s_odd, p_odd, p_even);
+      block(ic<SL1>{}, ic<SL>{}, 1, j1 * BC, s_even, s_odd, p_odd, p_even);
     }
 #pragma unroll
     for (int i = 0; i < NS; ++i) jq[i] = jq[i + 1];
@@ -323,7 +342,7 @@ __global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p)
 
   // Epilogue: O = O / l, lse = scale * m + ln(l).
   const float lt = half_swap_sum(l_run);
-  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  const float inv = lt > 0.f ? (DROP ? p.drop_scale : 1.0f) / lt : 0.f;
   const int q = q0w + l32;
   if (q < N) {
     T* orow = (T*)p.o + base + (size_t)q * D;
@@ -371,14 +390,14 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(FwdParams p) {
   int kt_end = (N + BC - 1) / BC;
   if (CAUSAL) kt_end = min(kt_end, (min(N, (qt + 1) * BR) + BC - 1) / BC);
   const uint8_t* mrow = SPARSE ? p.mask + (size_t)qt * p.mask_tiles : nullptr;
-  auto next_active = [&](int j) {
+  auto next_active = [&](int j) __attribute__((always_inline)) {
     if (SPARSE)
       while (j < kt_end && mrow[(j * BC) / MASK_TILE] == 0) ++j;
     return j;
   };
 
   float4 kreg[PT], vreg[PT];
-  auto gload = [&](int j) {
+  auto gload = [&](int j) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
       const int c = tid + 256 * u, row = c / CPR, col = (c % CPR) * 4;
@@ -392,7 +411,7 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(FwdParams p) {
       }
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
       const int c = tid + 256 * u, row = c / CPR, col = (c % CPR) * 4;
@@ -480,10 +499,16 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(FwdParams p) {
 template <typename T, int D>
 hipError_t launch16(const FwdParams& p, bool causal, bool sparse, hipStream_t st) {
   dim3 grid(((p.N + 127) / 128) * p.BH), block(256);
-  if (causal && sparse) fwd16_kernel<T, D, true, true><<<grid, block, 0, st>>>(p);
-  else if (causal) fwd16_kernel<T, D, true, false><<<grid, block, 0, st>>>(p);
-  else if (sparse) fwd16_kernel<T, D, false, true><<<grid, block, 0, st>>>(p);
-  else fwd16_kernel<T, D, false, false><<<grid, block, 0, st>>>(p);
+  const bool drop = p.drop_t8 > 0;
+  if (drop) {
+    if (causal && sparse) fwd16_kernel<T, D, true, true, true><<<grid, block, 0, st>>>(p);
+    else if (causal) fwd16_kernel<T, D, true, false, true><<<grid, block, 0, st>>>(p);
+    else if (sparse) fwd16_kernel<T, D, false, true, true><<<grid, block, 0, st>>>(p);
+    else fwd16_kernel<T, D, false, false, true><<<grid, block, 0, st>>>(p);
+  } else if (causal && sparse) fwd16_kernel<T, D, true, true, false><<<grid, block, 0, st>>>(p);
+  else if (causal) fwd16_kernel<T, D, true, false, false><<<grid, block, 0, st>>>(p);
+  else if (sparse) fwd16_kernel<T, D, false, true, false><<<grid, block, 0, st>>>(p);
+  else fwd16_kernel<T, D, false, false, false><<<grid, block, 0, st>>>(p);
   return hipGetLastError();
 }
 

@@ -42,6 +42,10 @@ struct FwdParams {
   int n_qtiles, n_ktiles, mask_tiles;
   float scale, scale_log2e;
   float rescale_thr;  // raw-score growth of the running max that forces a rescale
+  // Dropout (drop_t8 = 0: none): Philox key, counter word 3, byte threshold,
+  // 1 / (1 - drop_t8 / 256).
+  uint32_t drop_k0, drop_k1, drop_off, drop_t8;
+  float drop_scale;
 };
 
 struct BwdParams {
@@ -60,6 +64,8 @@ struct BwdParams {
   int BH, N;
   int n_ktiles, n_qtiles, mask_tiles;
   float scale, scale_log2e;
+  uint32_t drop_k0, drop_k1, drop_off, drop_t8;  // dropout as in FwdParams
+  float drop_scale;
 };
 
 struct DecParams {
@@ -96,9 +102,16 @@ struct Fp8Params {
   float scale_log2e, rsqrt_d;
 };
 
+struct DropMaskParams {
+  uint8_t* keep;   // (B*H, N, N): 1 = kept
+  int BH, N;
+  uint32_t k0, k1, off, t8;
+};
+
 hipError_t launch_forward(FwdParams p, int dtype, int d, bool causal, hipStream_t st);
 hipError_t launch_backward(BwdParams p, int dtype, int d, bool causal, hipStream_t st);
 hipError_t launch_decode(DecParams p, int dtype, int d, bool causal, hipStream_t st);
+hipError_t launch_dropout_mask(DropMaskParams p, hipStream_t st);
 hipError_t launch_fp8(Fp8Params p, int dtype, int d, bool causal, bool prep, bool attend,
                       hipStream_t st);
 

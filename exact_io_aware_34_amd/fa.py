@@ -45,6 +45,15 @@ _lib.fa_fp8_prepare.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, cty
 _lib.fa_fp8_prepare.restype = _i
 _lib.fa_forward_fp8_workspace_size.argtypes = [_i, _i, _i, _i]
 _lib.fa_forward_fp8_workspace_size.restype = ctypes.c_size_t
+_u64, _u32 = ctypes.c_uint64, ctypes.c_uint32
+_lib.fa_forward_dropout.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _i, _f,
+                                    _u64, _u32, _vp]
+_lib.fa_forward_dropout.restype = _i
+_lib.fa_backward_dropout.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
+                                     _f, _i, _vp, _i, _f, _u64, _u32, _vp, ctypes.c_size_t, _vp]
+_lib.fa_backward_dropout.restype = _i
+_lib.fa_dropout_mask.argtypes = [_i, _i, _i, _f, _u64, _u32, _vp, _vp]
+_lib.fa_dropout_mask.restype = _i
 _lib.fa_status_string.argtypes = [_i]
 _lib.fa_status_string.restype = ctypes.c_char_p
 _lib.fa_abi_version.restype = _i
@@ -108,8 +117,9 @@ def default_scale(d: int) -> float:
 
 
 def forward(q, k, v, causal=False, scale=None, block_mask=None, out=None, lse=None,
-            stream=None):
-    """Exact attention forward: returns (o, lse) with o in q's dtype, lse fp32."""
+            stream=None, dropout_p=0.0, seed=0, offset=0):
+    """Exact attention forward: returns (o, lse) with o in q's dtype, lse fp32.
+    dropout_p > 0 drops probabilities with the mask fa_dropout_mask describes."""
     _check_inputs(q, k, v)
     B, H, N, d = q.shape
     scale = default_scale(d) if scale is None else float(scale)
@@ -119,9 +129,14 @@ def forward(q, k, v, causal=False, scale=None, block_mask=None, out=None, lse=No
     _check_inputs(q, o)
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
         raise ValueError("lse must be contiguous float32 (B, H, N)")
-    rc = _lib.fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
-                         scale, int(bool(causal)), _ptr(mask), DTYPE_CODES[q.dtype],
-                         _stream(stream))
+    if dropout_p:
+        rc = _lib.fa_forward_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                                     scale, int(bool(causal)), _ptr(mask), DTYPE_CODES[q.dtype],
+                                     float(dropout_p), int(seed), int(offset), _stream(stream))
+    else:
+        rc = _lib.fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                             scale, int(bool(causal)), _ptr(mask), DTYPE_CODES[q.dtype],
+                             _stream(stream))
     if rc != 0:
         raise FAError(rc)
     return o, lse
@@ -132,8 +147,9 @@ def workspace_size(B, H, N, d) -> int:
 
 
 def backward(q, k, v, o, lse, do, causal=False, scale=None, block_mask=None,
-             workspace=None, grads=None, stream=None):
-    """Exact attention backward: returns fp32 (dq, dk, dv)."""
+             workspace=None, grads=None, stream=None, dropout_p=0.0, seed=0, offset=0):
+    """Exact attention backward: returns fp32 (dq, dk, dv).  With dropout,
+    pass the forward's (dropout_p, seed, offset) so the same mask applies."""
     _check_inputs(q, k, v, o, do)
     B, H, N, d = q.shape
     scale = default_scale(d) if scale is None else float(scale)
@@ -147,11 +163,18 @@ def backward(q, k, v, o, lse, do, causal=False, scale=None, block_mask=None,
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     dq, dk, dv = grads
-    rc = _lib.fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
-                          _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, scale,
-                          int(bool(causal)), _ptr(mask), DTYPE_CODES[q.dtype],
-                          _ptr(workspace), workspace.numel() * workspace.element_size(),
-                          _stream(stream))
+    ws_n = workspace.numel() * workspace.element_size()
+    if dropout_p:
+        rc = _lib.fa_backward_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                                      _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, scale,
+                                      int(bool(causal)), _ptr(mask), DTYPE_CODES[q.dtype],
+                                      float(dropout_p), int(seed), int(offset), _ptr(workspace),
+                                      ws_n, _stream(stream))
+    else:
+        rc = _lib.fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                              _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, scale,
+                              int(bool(causal)), _ptr(mask), DTYPE_CODES[q.dtype],
+                              _ptr(workspace), ws_n, _stream(stream))
     if rc != 0:
         raise FAError(rc)
     return dq, dk, dv
@@ -260,3 +283,13 @@ def forward_fp8(q, k, v, signs=None, causal=False, scale=None, block_mask=None, 
     if rc != 0:
         raise FAError(rc)
     return o, lse
+
+
+def dropout_mask(B, H, N, dropout_p, seed=0, offset=0, device="cuda", stream=None):
+    """The keep mask (B, H, N, N) uint8 that forward/backward apply."""
+    keep = torch.empty((B, H, N, N), dtype=torch.uint8, device=device)
+    rc = _lib.fa_dropout_mask(B, H, N, float(dropout_p), int(seed), int(offset), _ptr(keep),
+                              _stream(stream))
+    if rc != 0:
+        raise FAError(rc)
+    return keep

@@ -97,6 +97,47 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Dropout on the probabilities, fused into the same kernels.
+ *
+ * Dropout is one of the operations FlashAttention fuses into its kernel so
+ * that nothing N x N reaches HBM ("FlashAttention ... IO-Awareness" reading
+ * guide, xyznot.com, "Ideias centrais", "Fusão de Kernels"); the
+ * marketmaker.cc page passes `dropout_p` to the fused attention call
+ * ("L'intégration est de huit lignes").  With keep mask Z:
+ *   O = (P o Z) V / (1 - p),  lse as without dropout (statistic of P);
+ *   backward with the same Z: dV = (P o Z)^T dO / (1 - p),
+ *   dS = P o (Z o dP / (1 - p) - D),  D_i = sum_c dO_ic O_ic (O with dropout).
+ * Z is never stored: element (query i, key j) of head bh = b * H + h is kept
+ * iff byte (j mod 4) of word (i mod 4) of Philox-4x32-10 (Salmon, Moraes,
+ * Dror, Shaw, SC 2011) at counter (j div 4, i div 4, bh, offset) and key
+ * (seed mod 2^32, seed div 2^32) is >= t, t = min(255, floor(256 p + 1/2));
+ * kept values are scaled by 1 / (1 - t / 256).  Every kernel recomputes the
+ * bytes it needs, so forward and backward apply the same mask when called
+ * with the same (dropout_p, seed, offset).
+ *
+ * Arguments as fa_forward / fa_backward plus dropout_p (finite, 0 <= p < 1,
+ * else FA_ERR_INVALID_ARG), seed and offset.  p = 0 (t = 0) is the plain
+ * path.  FA_F32 with p > 0 -> FA_ERR_UNSUPPORTED.
+ */
+int fa_forward_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int N, int d, float scale, int causal,
+                       const uint8_t* block_mask, int dtype, float dropout_p, uint64_t seed,
+                       uint32_t offset, void* stream);
+
+int fa_backward_dropout(const void* q, const void* k, const void* v, const void* o,
+                        const void* dO, const float* lse, float* dq, float* dk, float* dv,
+                        int B, int H, int N, int d, float scale, int causal,
+                        const uint8_t* block_mask, int dtype, float dropout_p, uint64_t seed,
+                        uint32_t offset, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The keep mask the two calls above apply, written out: keep (device,
+ * (B, H, N, N) uint8, caller-owned) gets 1 for kept and 0 for dropped
+ * elements.  N <= 65536.  For inspection and tests; the attention calls never
+ * need it. */
+int fa_dropout_mask(int B, int H, int N, float dropout_p, uint64_t seed, uint32_t offset,
+                    uint8_t* keep, void* stream);
+
+/*
  * Decode: a few new queries against a long cached history.
  *
  * Decoding has one (or a few) new query rows and a long history of keys and

@@ -36,6 +36,11 @@ def lib():
     L.fa_fp8_prepare.argtypes = [vp, vp, vp, i, i, i, i, i, vp, vp, ctypes.c_size_t, vp]
     L.fa_forward_fp8_workspace_size.argtypes = [i, i, i, i]
     L.fa_forward_fp8_workspace_size.restype = ctypes.c_size_t
+    u64, u32 = ctypes.c_uint64, ctypes.c_uint32
+    L.fa_forward_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, f, u64, u32, vp]
+    L.fa_backward_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i,
+                                      f, u64, u32, vp, ctypes.c_size_t, vp]
+    L.fa_dropout_mask.argtypes = [i, i, i, f, u64, u32, vp, vp]
     return L
 
 
@@ -48,8 +53,9 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "fa_abi_version", "fa_backward", "fa_backward_workspace_size", "fa_decode",
-        "fa_decode_splits", "fa_decode_workspace_size", "fa_forward", "fa_forward_fp8",
-        "fa_forward_fp8_workspace_size", "fa_fp8_prepare", "fa_status_string"])
+        "fa_decode_splits", "fa_decode_workspace_size", "fa_dropout_mask", "fa_forward",
+        "fa_forward_dropout", "fa_forward_fp8", "fa_forward_fp8_workspace_size", "fa_fp8_prepare",
+        "fa_backward_dropout", "fa_status_string"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -200,3 +206,19 @@ def test_fp8_validation(lib):
     assert f8(lib, ws_bytes=need - 1) == -3
     assert lib.fa_fp8_prepare(FAKE, FAKE, FAKE, 2, 3, 100, 64, 2, None, None, 0, None) == -3
     assert lib.fa_fp8_prepare(None, FAKE, FAKE, 2, 3, 100, 64, 2, None, FAKE, need, None) == -1
+
+
+def test_dropout_validation(lib):
+    def fwd_d(p, dtype=2):
+        return lib.fa_forward_dropout(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 100, 64, 0.125, 0, None,
+                                      dtype, p, 1, 0, None)
+    assert fwd_d(-0.1) == -1
+    assert fwd_d(1.0) == -1
+    assert fwd_d(float("nan")) == -1
+    assert fwd_d(0.1, dtype=0) == -2                    # fp32 forward has no dropout
+    bwd_d = lib.fa_backward_dropout(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 100,
+                                    64, 0.125, 0, None, 2, 1.5, 1, 0, FAKE, 1 << 30, None)
+    assert bwd_d == -1
+    assert lib.fa_dropout_mask(1, 1, 10, 0.5, 1, 0, None, None) == -1
+    assert lib.fa_dropout_mask(1, 1, 10, 1.0, 1, 0, FAKE, None) == -1
+    assert lib.fa_dropout_mask(1, 1, 70000, 0.5, 1, 0, FAKE, None) == -2

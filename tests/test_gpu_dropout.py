@@ -1,0 +1,132 @@
+"""GPU parity of fused dropout (fa_forward_dropout, fa_backward_dropout,
+fa_dropout_mask) through the C ABI, against the dropout oracle.
+
+* The keep mask is integer work: fa_dropout_mask must equal the oracle's
+  Philox-4x32-10 mask bit for bit (several heads, ragged N, 64-bit seeds,
+  offsets, p = 0).
+* Forward and backward with dropout against oracle.forward_head_dropout /
+  backward_head_dropout on the same inputs, seed and offset -- the backward's
+  inputs include the forward's stored 16-bit O, which the oracle receives as
+  well (with dropout O = c sum P v is not exact in 16 bits even for a one-key
+  row, where dS = P (c dP - D) cancels exactly: the D computed from the
+  stored O leaves its rounding there, up to 2e-2 on dQ at d = 128, which is
+  what the same-input comparison removes).  Every kept term is the
+  non-dropout term times c = 1 / (1 - p), so the tolerance is the 16-bit
+  path's times c.  A mask that differed from the oracle's in even a few
+  elements would show up far above it.
+* p = 0 takes the plain path and matches it exactly.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_io_aware_34_amd import workloads as W
+from tests.parity import DT, LSE_TOL, TOL, assert_close, f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    from exact_io_aware_34_amd import fa as _fa
+    return _fa
+
+
+@pytest.mark.parametrize("B,H,N,p,seed,offset", [
+    (2, 3, 100, 0.3, (1 << 40) + 5, 7),
+    (1, 1, 1, 0.5, 3, 0),
+    (1, 2, 5, 0.1, 0xFFFFFFFFFFFFFFFF, 0xFFFFFFFF),
+    (1, 1, 64, 0.0, 9, 1),
+])
+def test_dropout_mask_bit_exact(fa, B, H, N, p, seed, offset):
+    keep = fa.dropout_mask(B, H, N, p, seed, offset).cpu().numpy()
+    r = np.arange(N)
+    for bh in range(B * H):
+        want = oracle.keep_mask(bh, r, r, seed, offset, p)
+        np.testing.assert_array_equal(keep.reshape(B * H, N, N)[bh], want.astype(np.uint8),
+                                      err_msg=f"bh={bh}")
+    if p == 0.0:
+        assert keep.all()
+
+
+def holed_mask(N, seed):
+    t = -(-N // 128)
+    g = torch.Generator().manual_seed(seed)
+    m = (torch.rand((t, t), generator=g) < 0.7).to(torch.uint8)
+    m[0, :] = 0
+    if t > 2:
+        m[1, 1] = 1
+    return m
+
+
+CASES = [
+    # B, H, N, d, dtype, causal, mask, p
+    (1, 2, 256, 64, "bf16", True, None, 0.1),
+    (1, 1, 300, 64, "f16", False, None, 0.5),
+    (2, 2, 130, 128, "bf16", True, None, 0.2),
+    (1, 2, 384, 64, "bf16", True, "holed", 0.3),
+    (1, 1, 449, 128, "f16", False, None, 0.25),
+    (1, 3, 64, 64, "f16", True, None, 0.4),
+]
+
+
+def _inputs(B, H, N, d, dtype, mask_kind):
+    q, k, v, do = W.draw_qkvdo(B, H, N, d, dtype, seed=11 * N + d)
+    mask = holed_mask(N, N) if mask_kind == "holed" else None
+    return q, k, v, do, mask
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype,causal,mask_kind,p", CASES)
+def test_dropout_forward_backward(fa, B, H, N, d, dtype, causal, mask_kind, p):
+    q, k, v, do, mask = _inputs(B, H, N, d, dtype, mask_kind)
+    seed, offset = 1234567 + N, 3
+    sc = W.scale_for(d)
+    md = None if mask is None else mask.cuda()
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=sc, block_mask=md, dropout_p=p,
+                        seed=seed, offset=offset)
+    dq, dk, dv = fa.backward(qd, kd, vd, o, lse, dod, causal=causal, scale=sc, block_mask=md,
+                             dropout_p=p, seed=seed, offset=offset)
+    torch.cuda.synchronize()
+    o, lse, dq, dk, dv = (t.cpu() for t in (o, lse, dq, dk, dv))
+    tol = TOL[DT[dtype]] * oracle.keep_scale(p)
+    mnp = None if mask is None else mask.numpy()
+    for b in range(B):
+        for h in range(H):
+            a = [f64(t[b, h]) for t in (q, k, v, do)]
+            ro, rl = oracle.forward_head_dropout(a[0], a[1], a[2], sc, p, seed, offset, b * H + h,
+                                                 causal, mnp)
+            assert_close(f"o[{b},{h}]", f64(o[b, h]), ro, tol)
+            assert_close(f"lse[{b},{h}]", f64(lse[b, h]), rl, LSE_TOL)
+            rq, rk, rv = oracle.backward_head_dropout(*a, sc, p, seed, offset, b * H + h, causal,
+                                                      mnp, o=f64(o[b, h]))
+            assert_close(f"dq[{b},{h}]", f64(dq[b, h]), rq, tol)
+            assert_close(f"dk[{b},{h}]", f64(dk[b, h]), rk, tol)
+            assert_close(f"dv[{b},{h}]", f64(dv[b, h]), rv, tol)
+    if mask_kind == "holed":
+        assert torch.all(o[:, :, :128] == 0) and torch.all(torch.isneginf(lse[:, :, :128]))
+
+
+def test_dropout_p0_is_the_plain_path(fa):
+    q, k, v, do, _ = _inputs(1, 2, 200, 64, "bf16", None)
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o0, l0 = fa.forward(qd, kd, vd, causal=True, dropout_p=0.0, seed=5)
+    o1, l1 = fa.forward(qd, kd, vd, causal=True)
+    g0 = fa.backward(qd, kd, vd, o0, l0, dod, causal=True, dropout_p=0.0, seed=5)
+    g1 = fa.backward(qd, kd, vd, o1, l1, dod, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    for a, b in zip(g0, g1):
+        assert torch.equal(a, b)
+
+
+def test_dropout_changes_with_seed_and_offset(fa):
+    q, k, v, do, _ = _inputs(1, 1, 128, 64, "bf16", None)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    outs = [fa.forward(qd, kd, vd, dropout_p=0.5, seed=s, offset=o)[0].clone()
+            for s, o in ((1, 0), (2, 0), (1, 1), (1, 0))]
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[3])                  # deterministic
+    assert not torch.equal(outs[0], outs[1]) and not torch.equal(outs[0], outs[2])

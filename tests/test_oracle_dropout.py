@@ -188,6 +188,21 @@ def test_backward_p0_is_plain_backward():
         np.testing.assert_allclose(a, b, atol=1e-13)
 
 
+def test_backward_takes_the_given_output():
+    n, d, p = 20, 8, 0.3
+    q, k, v, do = (RNG.standard_normal((n, d)) for _ in range(4))
+    o, _ = DR.forward_head_dropout(q, k, v, 0.3, p, 4, 0, 2, True)
+    a = DR.backward_head_dropout(q, k, v, do, 0.3, p, 4, 0, 2, True)
+    b = DR.backward_head_dropout(q, k, v, do, 0.3, p, 4, 0, 2, True, None, o)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(x, y, atol=1e-14)
+    # causal row 0 sees one key: dS_00 = c dP_00 - D_0 is exactly 0 with the
+    # exact O, and only an O that differs from it leaves dQ_0 non-zero.
+    assert np.abs(a[0][0]).max() < 1e-14
+    c = DR.backward_head_dropout(q, k, v, do, 0.3, p, 4, 0, 2, True, None, o * (1 + 1e-3))
+    assert np.abs(c[0][0]).max() > 1e-6 or not DR.keep_mask(2, [0], [0], 4, 0, p)[0, 0]
+
+
 # ---- planted slips ----
 
 def _bwd_mask_missing_in_dp(q, k, v, do, scale, p, seed, offset, bh, causal, mask):
