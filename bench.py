@@ -2,6 +2,7 @@
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                 [--calibrate-copy] [--decode-workload NAME | --no-decode] [--no-fp8]
+                [--no-dropout] [--dropout-p P]
 
 A step is one forward pass and one backward pass (every kernel of the path:
 forward, backward preprocess, backward main) over the workload's synthetic
@@ -15,6 +16,10 @@ is timed after the steps on its own workload and reported in the `decode`
 object of the same line: call time, algorithmic HBM bytes per call (16-bit K
 and V read once, q read, o and lse written) over that time against the
 8 TB/s HBM peak, and the oracle's rate on a few heads.
+
+The same step with fused dropout (fa_forward_dropout + fa_backward_dropout,
+probability 0.1 by default, a fixed seed) is timed after the plain steps and
+reported in the `dropout` object, with the same FLOP count.
 
 The FP8 forward (fa_forward_fp8: rotation + block quantisation, then
 attention on E4M3 operands) is timed on the same workload and reported in the
@@ -60,6 +65,8 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-cpu-heads", type=int, default=24)
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-dropout", action="store_true")
+    ap.add_argument("--dropout-p", type=float, default=0.1)
     ap.add_argument("--fp8-cpu-heads", type=int, default=2)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB device-to-device copy before the steps "
@@ -142,7 +149,7 @@ def cpu_baseline(w, inputs, n_heads):
     return out
 
 
-def time_passes(fa, w, tensors, mask, steps, warmup):
+def time_passes(fa, w, tensors, mask, steps, warmup, dropout_p=0.0, seed=0):
     """Per-step forward and backward times (ms, HIP events on the launch stream)."""
     import torch
     q, k, v, do, o, lse, ws, grads = tensors
@@ -151,12 +158,13 @@ def time_passes(fa, w, tensors, mask, steps, warmup):
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        fa.forward(q, k, v, causal=w.causal, scale=w.scale, block_mask=mask, out=o, lse=lse)
+        fa.forward(q, k, v, causal=w.causal, scale=w.scale, block_mask=mask, out=o, lse=lse,
+                   dropout_p=dropout_p, seed=seed)
         if ev is not None:
             ev[1].record(stream)
         if w.backward:
             fa.backward(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, block_mask=mask,
-                        workspace=ws, grads=grads)
+                        workspace=ws, grads=grads, dropout_p=dropout_p, seed=seed)
         if ev is not None:
             ev[2].record(stream)
 
@@ -322,6 +330,29 @@ def bench_fp8(fa, w, inputs, tensors, mask, steps, warmup, cpu_heads, with_cpu):
     return out
 
 
+def bench_dropout(fa, w, tensors, mask, steps, warmup, p, plain_ms):
+    mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
+    seed = 20260101
+    fwd_ms, bwd_ms, wall = time_passes(fa, w, tensors, mask, steps, warmup, dropout_p=p, seed=seed)
+    f_fwd, f_bwd = flops(w, mask.cpu() if mask is not None else None)
+    ms_step = wall * 1e3 / steps
+    tf_bwd = f_bwd / (mean(bwd_ms) * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    rec = recorded_traffic(w.name)
+    out = {"dropout_p": p, "seed": seed, "value": round((f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12, 2),
+           "unit": "TFLOPS", "ms_per_step": round(ms_step, 4),
+           "fwd_ms": round(mean(fwd_ms), 4), "bwd_ms": round(mean(bwd_ms), 4),
+           "fwd_tflops": round(f_fwd / (mean(fwd_ms) * 1e-3) / 1e12, 2),
+           "bwd_tflops": round(tf_bwd, 2),
+           "step_time_vs_plain": round(ms_step / plain_ms, 3),
+           "roofline": {"bound": "mfma", "kernel": "fa_backward_dropout (bwd_pre + bwd_dkdv + bwd_dq)",
+                        "achieved": round(tf_bwd, 2), "peak": peak, "unit": "TFLOP/s",
+                        "frac": round(tf_bwd / peak, 4),
+                        "traffic": None if rec is None else rec["bytes_per_call"].get("dropout_backward"),
+                        "avg_ms": round(mean(bwd_ms), 4)}}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -409,6 +440,9 @@ def main():
             "bwd": round(mean(d_bwd) / mean(bwd_ms) * kept, 4) if w.backward else None,
             "dense_fwd_ms": round(mean(d_fwd), 4),
             "dense_bwd_ms": round(mean(d_bwd), 4) if w.backward else None}
+    if not args.no_dropout and w.dtype in ("bf16", "f16") and w.backward:
+        out["dropout"] = bench_dropout(fa, w, tensors, mask, args.steps, args.warmup,
+                                       args.dropout_p, ms_step)
     if not args.no_fp8 and w.dtype in ("bf16", "f16"):
         out["fp8"] = bench_fp8(fa, w, inputs, tensors, mask, args.steps, args.warmup,
                                args.fp8_cpu_heads, not args.no_cpu_baseline)
