@@ -54,8 +54,11 @@ __device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c) {
 // Four fp32 values to four E4M3 bytes (a in the lowest byte).  The
 // conversion rounds to nearest even; it does not saturate, so every caller
 // keeps |x| <= 448.
+// Each conversion replaces one 16-bit half of its `old` operand; the low half
+// is written first over a's own bits, so no zeroed register is needed.
 __device__ __forceinline__ int pack_e4m3(float a, float b, float c, float d) {
-  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false), true);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
 __device__ __forceinline__ float quad_xor1(float x) {
@@ -203,8 +206,12 @@ __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
   constexpr int DB = D / 32;                 // O^T row blocks
   constexpr int CPR = D / 16;                // 16-byte chunks per K row
   constexpr int DMA_N = TB / 16 / 256;       // copies per wave per tile
+  constexpr int OPS = 2 * DMA_N + 1;         // copies per wave per tile (+ its two block scales)
   static_assert(BR == MASK_TILE, "a workgroup covers one block-mask row");
   __shared__ __attribute__((aligned(1024))) uint8_t kvs[2 * NS * TB];  // K slots, then V^T slots
+  // Block scales of the tile in each slot: [0] its K scale, [1] its V scale
+  // (lanes 2.. of the copy repeat them).
+  __shared__ __attribute__((aligned(16))) float sc_s[NS][64];
   __shared__ uint8_t mask_s[SPARSE ? FWD_MAX_MASK_TILES : 1];
   __shared__ float red_s[4];
 
@@ -238,6 +245,7 @@ __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
   if (lane == 0) red_s[wave] = mv;
   __syncthreads();
   const float sv_max = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
+  const float lsv_max = __log2f(sv_max);
 
   // Per-lane LDS byte offsets.  K (A operand of S^T): key 32 u + l32, bytes
   // 64 h + 32 g .. + 31.  V^T (A operand of O^T): row 32 db + l32, bytes
@@ -282,8 +290,10 @@ __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
   const int last_key = CAUSAL ? min(N - 1, q0w + 31) : N - 1;
   const int plain_key = CAUSAL ? min(N - 1, q0w) : N - 1;
 
-  // Copy K tile jj and V^T tile jj into slot `slot` (rows past N are zero
-  // in both: the preparation pads them).
+  // Copy K tile jj, V^T tile jj and their two block scales into slot `slot`
+  // (rows past N are zero in both tiles: the preparation pads them).  The
+  // scales travel with the tiles, so the wait that makes a tile visible
+  // covers them too.
   auto issue = [&](int jj, int slot) {
     const uint8_t* ks = K8 + (size_t)jj * TB;
     const uint8_t* vs = V8 + (size_t)jj * TB;
@@ -292,6 +302,7 @@ __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
     for (int u = 0; u < DMA_N; ++u) dma16_s(ks, kdo[u], kd + (uint32_t)((u * NW + wave) * 1024));
 #pragma unroll
     for (int u = 0; u < DMA_N; ++u) dma16_s(vs, vdo[u], vd + (uint32_t)((u * NW + wave) * 1024));
+    dma4((lane & 1) ? svh + jj : skh + jj, lds_addr(&sc_s[slot][0]));
   };
 
   int jq[NS];
@@ -323,7 +334,7 @@ __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
   int slot = 0;
   while (jq[0] < kt_end) {
     const int j = jq[0];
-    if (jq[1] < kt_end) wait_vmcnt<2 * DMA_N>();
+    if (jq[1] < kt_end) wait_vmcnt<OPS>();
     else wait_vmcnt<0>();
     wg_barrier();
     if (jq[2] < kt_end) issue(jq[2], slot == 0 ? 2 : slot - 1);
@@ -353,9 +364,10 @@ __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
             if (8 * (r >> 2) + (r & 3) > lim) s[u][r] = -INFINITY;
         }
       }
-      const float cj = c0 * skh[j];                       // raw accumulator -> log2 units
-      const float inv_r = sv_max / svh[j];                // 1 / r_t
-      const float lr = __log2f(svh[j] / sv_max);          // log2 r_t <= 0
+      const float2 sc = *(const float2*)&sc_s[slot][0];
+      const float cj = c0 * sc.x;                         // raw accumulator -> log2 units
+      const float lr = __log2f(sc.y) - lsv_max;           // log2 r_t <= 0
+      const float inv_r = fast_exp2(-lr);                 // 1 / r_t
       i32x8 pk;
       // p' = exp2(x - m_run) * r_t, packed to E4M3; returns the lane's sum of p'.
       auto exps = [&]() {
