@@ -1,0 +1,103 @@
+"""Calls on several HIP streams through the C ABI.
+
+fa.h promises that the library keeps no mutable global state, so calls on
+different streams may run concurrently, and that every call enqueues its work
+on the stream it is given.  The forward, backward and decode kernels have no
+atomics and a fixed reduction order, so each result is bit-for-bit the same
+however the calls interleave:
+
+* two different problems, each repeated on its own side stream and issued
+  back to back, give exactly the results of the same calls run one after the
+  other on the current stream;
+* a call on a side stream sees what earlier work on that stream wrote (its
+  input is produced by a copy queued behind a long matrix product on the same
+  stream), so it is ordered on that stream and not on another one;
+* decode and the FP8 forward, which take caller-owned workspaces, give the
+  serial results when two calls with separate workspaces overlap.
+"""
+
+import pytest
+import torch
+
+from exact_io_aware_34_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    from exact_io_aware_34_amd import fa as _fa
+    return _fa
+
+
+def _inputs(B, H, N, d, dtype, seed):
+    return [t.cuda() for t in W.draw_qkvdo(B, H, N, d, dtype, seed=seed)]
+
+
+def _step(fa, q, k, v, do, causal):
+    o, lse = fa.forward(q, k, v, causal=causal)
+    dq, dk, dv = fa.backward(q, k, v, o, lse, do, causal=causal)
+    return o, lse, dq, dk, dv
+
+
+PROBLEMS = [(1, 2, 640, 64, "bf16", True, 1), (1, 2, 520, 128, "f16", False, 2)]
+
+
+def test_concurrent_streams_match_serial(fa):
+    inputs = [(_inputs(B, H, N, d, dt, seed), causal) for B, H, N, d, dt, causal, seed in PROBLEMS]
+    ref = [_step(fa, *x, causal) for x, causal in inputs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in inputs]
+    got = [[] for _ in inputs]
+    for _ in range(3):
+        for i, (s, (x, causal)) in enumerate(zip(streams, inputs)):
+            with torch.cuda.stream(s):
+                got[i].append(_step(fa, *x, causal))
+    torch.cuda.synchronize()
+    names = ("o", "lse", "dq", "dk", "dv")
+    for i in range(len(inputs)):
+        for rep in got[i]:
+            for name, a, b in zip(names, rep, ref[i]):
+                assert torch.equal(a, b), f"problem {i}: {name} differs from the serial result"
+
+
+def test_call_is_ordered_on_its_stream(fa):
+    q, k, v, _ = _inputs(1, 2, 384, 64, "bf16", 3)
+    o_ref, lse_ref = fa.forward(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    big = torch.randn(4096, 4096, device="cuda")
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(4):
+            big = big @ big * 1e-3              # keeps the stream busy before the copy
+        q2 = torch.empty_like(q)
+        q2.copy_(q)
+        o, lse = fa.forward(q2, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref)
+
+
+def test_workspace_calls_on_two_streams(fa):
+    d = 64
+    dq_, dk_, dv_ = (t.cuda() for t in W.draw_decode(2, 2, 3, 1500, d, "bf16", seed=4))
+    ws_size = fa.decode_workspace_size(2, 2, 3, 1500, d, 4)
+    ref = fa.decode(dq_, dk_, dv_, causal=True, n_splits=4)
+    q, k, v, _ = _inputs(1, 2, 500, d, "bf16", 5)
+    signs = W.draw_rotation_signs(d, seed=6).cuda()
+    ref8 = fa.forward_fp8(q, k, v, signs=signs, causal=True)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            ws1 = torch.empty(ws_size, dtype=torch.uint8, device="cuda")
+            outs.append(("decode", fa.decode(dq_, dk_, dv_, causal=True, n_splits=4, workspace=ws1),
+                         ref))
+        with torch.cuda.stream(s2):
+            ws2 = torch.empty(fa.fp8_workspace_size(1, 2, 500, d), dtype=torch.uint8, device="cuda")
+            outs.append(("fp8", fa.forward_fp8(q, k, v, signs=signs, causal=True, workspace=ws2),
+                         ref8))
+    torch.cuda.synchronize()
+    for name, (o, lse), (ro, rl) in outs:
+        assert torch.equal(o, ro) and torch.equal(lse, rl), f"{name} differs from the serial result"
