@@ -5,14 +5,16 @@ a head count that is not a multiple of the eight XCDs (the causal grids map
 workgroups to heads round robin); block masks with an empty row (queries that
 see no key: O = 0, lse = -inf, dQ = 0) and an empty column (keys no query
 sees: dK = dV = 0), alone and combined with causal masking; a scale other
-than 1/sqrt(d).  Each case is compared element by element with the fp64
-oracle on the same rounded inputs.
+than 1/sqrt(d); the largest block-mask grid (2048 x 2048 tiles) at a ragged
+N.  Each case is compared element by element with the fp64 oracle on the
+same rounded inputs.
 """
 
 import numpy as np
 import pytest
 import torch
 
+import oracle
 from exact_io_aware_34_amd import workloads as W
 from tests.parity import (DT, LSE_TOL, TOL, assert_close, f64, oracle_backward_heads,
                           oracle_forward_heads)
@@ -98,3 +100,40 @@ def test_edges_backward(fa, B, H, N, d, dtype, causal, mask_kind, scale):
         assert torch.all(dk[:, :, (t - 1) * 128:] == 0)
         assert torch.all(dv[:, :, (t - 1) * 128:] == 0)
     assert np.isfinite(dq.numpy()).all() and np.isfinite(dk.numpy()).all()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_largest_mask_grid_block_diagonal(fa, causal):
+    """The largest block mask the kernels accept (2048 x 2048 tiles) at a
+    ragged N = 262100 (last tile 84 rows), with only the diagonal tiles set.
+    Query tile t then sees exactly key tile t, and key tile t receives
+    gradient only from query tile t, so every tile is an independent
+    attention problem of at most 128 rows: sampled tiles (first, second,
+    middle, last two) are compared element by element with the oracle run
+    on that tile alone, forward and backward."""
+    B, H, N, d, dtype = 1, 2, 262100, 64, "bf16"
+    t = -(-N // 128)
+    assert t == 2048
+    q, k, v, do = W.draw_qkvdo(B, H, N, d, dtype, seed=101)
+    sc = W.scale_for(d)
+    mask = torch.eye(t, dtype=torch.uint8)
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=sc, block_mask=mask.cuda())
+    dq, dk, dv = fa.backward(qd, kd, vd, o, lse, dod, causal=causal, scale=sc,
+                             block_mask=mask.cuda())
+    torch.cuda.synchronize()
+    tol = TOL[DT[dtype]]
+    for tile in (0, 1, 1023, t - 2, t - 1):
+        r = slice(128 * tile, min(N, 128 * (tile + 1)))
+        for h in range(H):
+            a = [f64(x[0, h, r]) for x in (q, k, v, do)]
+            ro, rl = oracle.forward_head(a[0], a[1], a[2], sc, causal=causal)
+            rq, rk, rv = oracle.backward_head(*a, sc, causal=causal)
+            tag = f"tile {tile} head {h}"
+            assert_close(f"o {tag}", f64(o[0, h, r].cpu()), ro, tol)
+            assert_close(f"lse {tag}", f64(lse[0, h, r].cpu()), rl, LSE_TOL)
+            assert_close(f"dq {tag}", f64(dq[0, h, r].cpu()), rq, tol)
+            assert_close(f"dk {tag}", f64(dk[0, h, r].cpu()), rk, tol)
+            assert_close(f"dv {tag}", f64(dv[0, h, r].cpu()), rv, tol)
+    for x in (o, lse, dq, dk, dv):
+        assert torch.isfinite(x).all()
