@@ -217,7 +217,7 @@ extern "C" {
 
 size_t fa_backward_workspace_size(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
-  return 2 * delta_bytes(B, H, N);  // D and the log2-domain lse, one fp32 each per row
+  return 2 * delta_bytes(B, H, N);  // -D and the log2-domain lse, one fp32 each per row
 }
 
 int fa_backward(const void* q, const void* k, const void* v, const void* o,
@@ -284,7 +284,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
-  p.delta = (float*)workspace;
+  p.neg_delta = (float*)workspace;
   p.lse2 = (float*)((char*)workspace + delta_bytes(B, H, N));
   p.mask = block_mask;
   p.BH = B * H;

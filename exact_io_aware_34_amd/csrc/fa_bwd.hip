@@ -9,7 +9,7 @@
 //   D_i = sum_c dO_ic O_ic,  dS = P o (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
 //
 // Three kernels, no atomics:
-//   bwd_pre:  per row, D = rowsum(dO o O) and the log2-domain statistic
+//   bwd_pre:  per row, -D = -rowsum(dO o O) and the log2-domain statistic
 //     lse * log2(e) (+inf for rows with no visible key, so P = 0 there), both
 //     fp32, into the workspace.
 //   bwd_dkdv_u: one workgroup per (key tile of 128, batch*head).  Wave w owns
@@ -45,7 +45,7 @@ using ic = std::integral_constant<int, V>;
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO,
                                                       const float* __restrict__ lse,
-                                                      float* __restrict__ delta, float* __restrict__ lse2,
+                                                      float* __restrict__ neg_delta, float* __restrict__ lse2,
                                                       size_t rows) {
   using VT = typename V8<T>::t;
   constexpr int LPR = D / 8;  // lanes per row, 8 elements each
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, c
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (row < rows && part == 0) {
-    delta[row] = acc;
+    neg_delta[row] = -acc;
     const float l = lse[row];
     lse2[row] = l == -INFINITY ? INFINITY : l * kLog2e;
   }
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdPara
   const T* __restrict__ V = (const T*)p.v + base;
   const T* __restrict__ dO = (const T*)p.dO + base;
   const float* __restrict__ L2 = p.lse2 + (size_t)bh * N;
-  const float* __restrict__ DEL = p.delta + (size_t)bh * N;
+  const float* __restrict__ NDEL = p.neg_delta + (size_t)bh * N;
   const int k0 = j * BC, kw0 = k0 + 32 * wave, my_k = kw0 + l32;
   const float c = p.scale_log2e;
 
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdPara
       }
     }
     const int qs = min(qa + lane, N - 1);
-    dma4((wave & 1) ? DEL + qs : L2 + qs, sd);
+    dma4((wave & 1) ? NDEL + qs : L2 + qs, sd);
   };
 
   VT kf[DS], vf[DS];
@@ -214,11 +214,25 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdPara
   }
 
   // S = Q K^T and dP = dO V^T of half h of the tile in slot SL: lane = key,
-  // register r = query 32h + 8(r/4) + 4g + r%4 of the tile.
+  // register r = query 32h + 8(r/4) + 4g + r%4 of the tile.  Without
+  // dropout the dP accumulator starts at -D of its query row, so it ends
+  // holding dP - D, the factor dS needs.
   auto sdp = [&](int slot, int h, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
     const T* qt_ = lds + slot * STAGE + 32 * h * D;
     s = f32x16{};
-    dp = f32x16{};
+    if constexpr (DROP) {
+      dp = f32x16{};
+    } else {
+      const float* nd = &st_s[slot][QT + 32 * h];
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const float4 v4 = *(const float4*)(nd + 8 * rg + 4 * g);
+        dp[4 * rg] = v4.x;
+        dp[4 * rg + 1] = v4.y;
+        dp[4 * rg + 2] = v4.z;
+        dp[4 * rg + 3] = v4.w;
+      }
+    }
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
       s = mfma32x32x16(*(const VT*)(qt_ + aoff[ds]), kf[ds], s);
@@ -240,10 +254,11 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdPara
         dk[db] = mfma32x32x16(dsa[kk], qfr, dk[db]);
       }
   };
-  // P and dS of half h of the tile in slot SL, rounded to 16-bit operands.
-  // With dropout (queries qb + 8t + 4g + e of the unit, this lane's key):
-  // P^T for dV keeps only the kept probabilities (1 / (1 - p) is applied to
-  // dV at the end) and dS = P o (Z dP / (1 - p) - D).
+  // P and dS of half h of the tile in slot SL, rounded to 16-bit operands;
+  // dp holds dP - D (see sdp).  With dropout it holds dP, and (queries
+  // qb + 8t + 4g + e of the unit, this lane's key) P^T for dV keeps only the
+  // kept probabilities (1 / (1 - p) is applied to dV at the end) and
+  // dS = P o (Z dP / (1 - p) - D).
   auto pds = [&](int slot, int h, int qb, const f32x16& s, const f32x16& dp, VT (&pa)[2],
                  VT (&dsa)[2]) __attribute__((always_inline)) {
     const float* sf = &st_s[slot][32 * h];
@@ -253,19 +268,18 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdPara
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
       const float4 l4 = *(const float4*)(sf + 8 * rg + 4 * g);
-      const float4 d4 = *(const float4*)(sf + QT + 8 * rg + 4 * g);
       const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-      const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
       float pv[4], dsv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         pv[e] = fast_exp2(fmaf(s[4 * rg + e], c, -lv[e]));
         if constexpr (DROP) {
+          const float nd = sf[QT + 8 * rg + 4 * g + e];    // -D
           const bool kp = drop_keep(dwk, 4 * rg + e, p.drop_t8);
-          dsv[e] = pv[e] * ((kp ? dp[4 * rg + e] * p.drop_scale : 0.f) - dd[e]);
+          dsv[e] = pv[e] * ((kp ? dp[4 * rg + e] * p.drop_scale : 0.f) + nd);
           pv[e] = kp ? pv[e] : 0.f;
         } else {
-          dsv[e] = pv[e] * (dp[4 * rg + e] - dd[e]);
+          dsv[e] = pv[e] * dp[4 * rg + e];
         }
       }
       const int kk = rg >> 1, w0 = 2 * (rg & 1);
@@ -488,7 +502,7 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dq_u_kernel(BwdParams
   }
   // +inf statistic makes P = 0 on padding rows.
   const float lq = my_q < N ? p.lse2[(size_t)bh * N + my_q] : INFINITY;
-  const float dq_row = my_q < N ? p.delta[(size_t)bh * N + my_q] : 0.f;
+  const float nd_row = my_q < N ? p.neg_delta[(size_t)bh * N + my_q] : 0.f;  // -D
 
   f32x16 acc[DB];
 #pragma unroll
@@ -538,7 +552,7 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dq_u_kernel(BwdParams
           d0 = drop_keep(dwq, r, p.drop_t8) ? d0 * p.drop_scale : 0.f;
           d1 = drop_keep(dwq, r + 1, p.drop_t8) ? d1 * p.drop_scale : 0.f;
         }
-        w[e] = pack2<T>(p0 * (d0 - dq_row), p1 * (d1 - dq_row));
+        w[e] = pack2<T>(p0 * (d0 + nd_row), p1 * (d1 + nd_row));
       }
       dsf[h] = __builtin_bit_cast(VT, w);
     }
@@ -634,7 +648,7 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
   const size_t rows = (size_t)p.BH * p.N;
   const size_t threads = rows * (D / 8);
   bwd_pre_kernel<T, D><<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st>>>(
-      (const T*)p.o, (const T*)p.dO, p.lse, p.delta, p.lse2, rows);
+      (const T*)p.o, (const T*)p.dO, p.lse, p.neg_delta, p.lse2, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid(((p.N + 127) / 128) * p.BH), block(256);

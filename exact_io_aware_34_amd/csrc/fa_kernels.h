@@ -58,7 +58,7 @@ struct BwdParams {
   float* dq;
   float* dk;
   float* dv;
-  float* delta;  // workspace: D_i = sum_c dO_ic o_ic, (B*H, N)
+  float* neg_delta;  // workspace: -D_i = -sum_c dO_ic o_ic, (B*H, N)
   float* lse2;   // workspace: lse_i * log2(e), +inf for rows with no visible key
   const uint8_t* mask;
   int BH, N;
