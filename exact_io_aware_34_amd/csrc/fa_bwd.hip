@@ -269,14 +269,21 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdPara
     for (int rg = 0; rg < 4; ++rg) {
       const float4 l4 = *(const float4*)(sf + 8 * rg + 4 * g);
       const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      float nd[4] = {};                                    // -D (dropout only)
+      if constexpr (DROP) {
+        const float4 d4 = *(const float4*)(sf + QT + 8 * rg + 4 * g);
+        nd[0] = d4.x;
+        nd[1] = d4.y;
+        nd[2] = d4.z;
+        nd[3] = d4.w;
+      }
       float pv[4], dsv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         pv[e] = fast_exp2(fmaf(s[4 * rg + e], c, -lv[e]));
         if constexpr (DROP) {
-          const float nd = sf[QT + 8 * rg + 4 * g + e];    // -D
           const bool kp = drop_keep(dwk, 4 * rg + e, p.drop_t8);
-          dsv[e] = pv[e] * ((kp ? dp[4 * rg + e] * p.drop_scale : 0.f) + nd);
+          dsv[e] = pv[e] * ((kp ? dp[4 * rg + e] * p.drop_scale : 0.f) + nd[e]);
           pv[e] = kp ? pv[e] : 0.f;
         } else {
           dsv[e] = pv[e] * dp[4 * rg + e];
