@@ -372,7 +372,7 @@ __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
       // p' = exp2(x - m_run) * r_t, packed to E4M3; returns the lane's sum of p'.
       auto exps = [&]() {
         const float off = lr - m_run;
-        float ls0 = 0.f, ls1 = 0.f;
+        float ls0, ls1;  // start at the first terms, not at 0
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -380,8 +380,9 @@ __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
             float e[4];
 #pragma unroll
             for (int b = 0; b < 4; ++b) e[b] = fast_exp2(fmaf(s[u][4 * w4 + b], cj, off));
-            ls0 += e[0] + e[1];
-            ls1 += e[2] + e[3];
+            const bool first = u == 0 && w4 == 0;
+            ls0 = first ? e[0] + e[1] : ls0 + (e[0] + e[1]);
+            ls1 = first ? e[2] + e[3] : ls1 + (e[2] + e[3]);
             pk[4 * u + w4] = pack_e4m3(e[0], e[1], e[2], e[3]);
           }
         return ls0 + ls1;

@@ -173,6 +173,7 @@ __global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p)
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   float m_run = -1e30f, l_run = 0.f;
+  float mc_run = m_run * c;  // m_run * c, updated with m_run
 
   // ---- work on one 32-key unit ----
   // S^T[key][query] of half h of the K tile in slot SL.
@@ -199,8 +200,9 @@ __global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p)
   // With dropout the row sum takes every exponential and the P V operand
   // only the kept ones (the 1 / (1 - p) scale is applied at the end).
   auto exps = [&](const f32x16& s, VT (&pu)[2], const uint32_t (&dw)[4]) __attribute__((always_inline)) {
-    const float mc = m_run * c;
-    float ls0 = 0.f, ls1 = 0.f;
+    const float mc = mc_run;
+    // The sums start at the first terms (not at 0, which would cost an add).
+    float ls0, ls1;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       u32x4 w;
@@ -209,8 +211,8 @@ __global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p)
         const int r = 8 * h + 2 * e;
         float e0 = fast_exp2(fmaf(s[r], c, -mc));
         float e1 = fast_exp2(fmaf(s[r + 1], c, -mc));
-        ls0 += e0;
-        ls1 += e1;
+        ls0 = r == 0 ? e0 : ls0 + e0;
+        ls1 = r == 0 ? e1 : ls1 + e1;
         if constexpr (DROP) {
           e0 = drop_keep(dw, r, p.drop_t8) ? e0 : 0.f;
           e1 = drop_keep(dw, r + 1, p.drop_t8) ? e1 : 0.f;
@@ -236,6 +238,7 @@ __global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p)
       const float m_new = fmaxf(m_run, half_swap_max(mx));
       const float alpha = fast_exp2((m_run - m_new) * c);
       m_run = m_new;
+      mc_run = m_new * c;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
