@@ -343,6 +343,10 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdPara
     sdp(0, 1, s_odd, dp_odd);
     pds(0, 0, iq[0] * QT, s_even, dp_even, pa_even, ds_even);
   }
+  // K, V rows and the statistics were ordinary loads: drain them here, where
+  // the compiler sees it, so that it places no vmcnt wait (which would also
+  // wait for the copies in flight) at their first use inside the loop.
+  wait_all_loads();
   // One iteration; the slot is a run-time index (four unrolled copies with
   // constant slots need more registers than the occupancy allows).  MASKED
   // iterations apply the edge masks; the others are branch-free between
@@ -602,6 +606,10 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dq_u_kernel(BwdParams
     sdp(0, 0, 1, s_odd, dp_odd);
     dscores(jq[0] * BC, s_even, dp_even, ds_even);
   }
+  // Q, dO rows and the row statistics were ordinary loads: drain them where
+  // the compiler sees it (no vmcnt wait on the copies in flight inside the
+  // loop).
+  wait_all_loads();
   // One iteration; the slots are run-time indices (K: n mod 4, V: n mod 3).
   // MASKED iterations apply the edge masks; the others are branch-free
   // between their two blocks.

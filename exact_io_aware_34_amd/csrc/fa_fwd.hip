@@ -309,6 +309,10 @@ __global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p)
     drop_words(jq[0] * BC, dw);
     settle(exps(s_even, p_even, dw), s_even, p_even, dw);
   }
+  // The Q^T fragments were ordinary loads: drain them where the compiler
+  // sees it, so that their first use inside the loop gets no vmcnt wait
+  // (which would also wait for the K/V copies in flight).
+  wait_all_loads();
   auto iter = [&](auto slc) __attribute__((always_inline)) {
     constexpr int SL = decltype(slc)::value;        // n % NS
     constexpr int SL1 = (SL + 1) % NS;              // slot of tile n+1
