@@ -23,6 +23,10 @@ The same step with fused dropout (fa_forward_dropout + fa_backward_dropout,
 probability 0.1 by default, a fixed seed) is timed after the plain steps and
 reported in the `dropout` object, with the same FLOP count.
 
+On workloads whose forward grid is too small to fill the GPU (16-bit inputs,
+fewer than 512 query tiles in all), the `split_forward` object times
+fa_forward_split with the library's number of key runs.
+
 The FP8 forward (fa_forward_fp8: rotation + block quantisation, then
 attention on E4M3 operands) is timed on the same workload and reported in the
 `fp8` object: call time (both kernels) and the preparation alone, the
@@ -287,6 +291,43 @@ def fp8_cpu_baseline(w, inputs, signs, n_heads):
                       f"os.cpu_count()={os.cpu_count()}"}
 
 
+def bench_split(fa, w, tensors, mask, steps, warmup, fwd_ms):
+    """fa_forward_split with the library's run count, for workloads whose
+    plain forward grid is too small to fill the GPU."""
+    import torch
+    q, k, v, _, o, lse, _, _ = tensors
+    n = fa.forward_splits(w.B, w.H, w.N, w.d, 0)
+    ws = torch.empty(max(1, fa.forward_split_workspace_size(w.B, w.H, w.N, w.d, 0)),
+                     dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        fa.forward(q, k, v, causal=w.causal, scale=w.scale, block_mask=mask, out=o, lse=lse,
+                   n_splits=0, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    mean = sum(ms) / len(ms)
+    f_fwd, _ = flops(w, mask.cpu() if mask is not None else None)
+    tf = f_fwd / (mean * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    return {"n_splits": n, "workgroups": ((w.N + 127) // 128) * w.B * w.H * n,
+            "ms": round(mean, 4),
+            "ms_median_min": [round(statistics.median(ms), 4), round(min(ms), 4)],
+            "tflops": round(tf, 2), "frac_peak": round(tf / peak, 4),
+            "vs_plain_forward": round(fwd_ms / mean, 3),
+            "kernels": "fwd16 over key runs + dec_combine merge"}
+
+
 def bench_fp8(fa, w, inputs, tensors, mask, steps, warmup, cpu_heads, with_cpu):
     import torch
 
@@ -442,6 +483,9 @@ def main():
             "bwd": round(mean(d_bwd) / mean(bwd_ms) * kept, 4) if w.backward else None,
             "dense_fwd_ms": round(mean(d_fwd), 4),
             "dense_bwd_ms": round(mean(d_bwd), 4) if w.backward else None}
+    if w.dtype in ("bf16", "f16") and fa.forward_splits(B, H, N, d, 0) > 1:
+        out["split_forward"] = bench_split(fa, w, tensors, mask, args.steps, args.warmup,
+                                           mean(fwd_ms))
     if not args.no_dropout and w.dtype in ("bf16", "f16") and w.backward:
         out["dropout"] = bench_dropout(fa, w, tensors, mask, args.steps, args.warmup,
                                        args.dropout_p, ms_step)

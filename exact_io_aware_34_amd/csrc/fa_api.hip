@@ -11,6 +11,7 @@
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxForwardSplits = 64;  // key ranges per query tile in fa_forward_split
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -211,9 +212,99 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+// Key runs of the split forward.  n_splits = 0 picks a count for grids
+// smaller than one full round of workgroups (768 at d = 64: three per CU;
+// 512 at d = 128: two): enough (query tile, run) workgroups for one round,
+// with runs of at least ten 64-key tiles.  A sweep of the count on one to
+// four heads of N = 4096..16384 found the fastest counts within 7 % of this
+// choice (runs shorter than ~10 tiles spend most of their time filling and
+// draining the copy pipeline).  An explicit count is capped at the number of
+// 64-key tiles.
+int forward_split_count(int B, int H, int N, int d, int n_splits) {
+  if (B < 1 || H < 1 || N < 1 || n_splits < 0 || (d != 64 && d != 128)) return 0;
+  const long long n_kt = (N + 63) / 64;
+  const long long wgs = (long long)B * H * ((N + 127) / 128);
+  const long long round = d == 64 ? 768 : 512;
+  long long n = n_splits;
+  if (n == 0) {
+    n = 1;
+    if (wgs < round) n = std::min((round + wgs - 1) / wgs, std::max(1LL, n_kt / 10));
+  }
+  n = std::min(n, std::min(n_kt, (long long)kMaxForwardSplits));
+  return (int)std::max(1LL, n);
+}
+
+size_t forward_split_part_bytes(int B, int H, int N, int d, int n) {
+  return pad256((size_t)B * H * n * N * d * sizeof(float));
+}
+
 }  // namespace
 
 extern "C" {
+
+int fa_forward_splits(int B, int H, int N, int d, int n_splits) {
+  return forward_split_count(B, H, N, d, n_splits);
+}
+
+size_t fa_forward_split_workspace_size(int B, int H, int N, int d, int n_splits) {
+  const int n = forward_split_count(B, H, N, d, n_splits);
+  if (n <= 1) return 0;
+  return forward_split_part_bytes(B, H, N, d, n) + pad256((size_t)B * H * n * N * sizeof(float));
+}
+
+int fa_forward_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int N, int d, float scale, int causal,
+                     const uint8_t* block_mask, int dtype, int n_splits, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (n_splits < 0) return FA_ERR_INVALID_ARG;
+  const int rc = check_common(B, H, N, d, scale, dtype);
+  if (rc != FA_OK) return rc;
+  const int n = forward_split_count(B, H, N, d, n_splits);
+  if (n <= 1 || (dtype == FA_F32 && n_splits == 0))
+    return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, dtype, 0.f, 0, 0,
+                        stream);
+  if (!tensor_ptr_ok(q) || !tensor_ptr_ok(k) || !tensor_ptr_ok(v) || !tensor_ptr_ok(o))
+    return FA_ERR_INVALID_ARG;
+  if (lse == nullptr || !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (block_mask != nullptr && (N + fa::MASK_TILE - 1) / fa::MASK_TILE > fa::FWD_MAX_MASK_TILES)
+    return FA_ERR_UNSUPPORTED;
+  // Partial rows and the split grid are indexed with int in the kernels.
+  const long long rows = (long long)B * H * n * N;
+  if (rows > (1LL << 31) - 1 || (long long)B * H * n * ((N + 127) / 128) > (1LL << 31) - 1)
+    return FA_ERR_UNSUPPORTED;
+  const size_t need = fa_forward_split_workspace_size(B, H, N, d, n_splits);
+  if (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < need)
+    return FA_ERR_WORKSPACE;
+  fa::FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.mask = block_mask;
+  p.BH = B * H;
+  p.N = N;
+  p.mask_tiles = (N + fa::MASK_TILE - 1) / fa::MASK_TILE;
+  p.scale = scale;
+  p.scale_log2e = scale * kLog2e;
+  p.rescale_thr = 8.0f / p.scale_log2e;
+  p.n_splits = n;
+  p.o_part = (float*)workspace;
+  p.lse_part = (float*)((char*)workspace + forward_split_part_bytes(B, H, N, d, n));
+  hipError_t e = fa::launch_forward(p, dtype, d, causal != 0, (hipStream_t)stream);
+  if (e != hipSuccess) return FA_ERR_HIP;
+  fa::DecParams m{};
+  m.o = o;
+  m.lse = lse;
+  m.o_part = p.o_part;
+  m.lse_part = p.lse_part;
+  m.BH = B * H;
+  m.Nq = N;
+  m.n_splits = n;
+  e = fa::launch_split_merge(m, dtype, d, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
 
 size_t fa_backward_workspace_size(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return 0;

@@ -328,6 +328,19 @@ hipError_t launch_dec_dt(const DecParams& p, int d, bool causal, hipStream_t st)
 
 }  // namespace
 
+hipError_t launch_split_merge(DecParams p, int dtype, int d, hipStream_t st) {
+  const int rows = p.BH * p.Nq, rpb = 256 / d;
+  const dim3 grid((unsigned)((rows + rpb - 1) / rpb));
+  if (dtype == DT_BF16) {
+    if (d == 64) hipLaunchKernelGGL((dec_combine_kernel<__bf16, 64>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((dec_combine_kernel<__bf16, 128>), grid, dim3(256), 0, st, p);
+  } else {
+    if (d == 64) hipLaunchKernelGGL((dec_combine_kernel<_Float16, 64>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((dec_combine_kernel<_Float16, 128>), grid, dim3(256), 0, st, p);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(DecParams p, int dtype, int d, bool causal, hipStream_t st) {
   if (dtype == DT_BF16) return launch_dec_dt<__bf16>(p, d, causal, st);
   return launch_dec_dt<_Float16>(p, d, causal, st);

@@ -61,15 +61,23 @@ __global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p)
   const int g = lane >> 5, l32 = lane & 31, s16 = lane & 15, gq = lane >> 4;
   const int N = p.N;
   const int n_qt = (N + BR - 1) / BR;
+  // Split key ranges: consecutive workgroups share a query tile, one range
+  // each (n_splits = 1: the whole range).
+  const int n_sp = p.n_splits;
+  int bid = blockIdx.x, split = 0;
+  if (n_sp > 1) {
+    split = bid % n_sp;
+    bid /= n_sp;
+  }
   int bh, qt;
   if (CAUSAL) {
     // Longest query tiles first across all heads (a list schedule in order
     // of decreasing work); with B*H a multiple of 8 the round-robin XCD
     // assignment still gives every XCD whole heads.
-    bh = blockIdx.x % p.BH;
-    qt = n_qt - 1 - blockIdx.x / p.BH;
+    bh = bid % p.BH;
+    qt = n_qt - 1 - bid / p.BH;
   } else {
-    const int lid = xcd_remap(blockIdx.x, n_qt * p.BH);
+    const int lid = xcd_remap(bid, n_qt * p.BH);
     bh = lid / n_qt;
     qt = lid - bh * n_qt;
   }
@@ -113,6 +121,13 @@ __global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p)
   const int n_kt = (N + BC - 1) / BC;
   int kt_end = n_kt;
   if (CAUSAL) kt_end = min(kt_end, (min(N, (qt + 1) * BR) + BC - 1) / BC);
+  // This workgroup's run of key tiles: [kt_begin, kt_end).
+  int kt_begin = 0;
+  if (n_sp > 1) {
+    const int all = kt_end;
+    kt_begin = (int)((long long)all * split / n_sp);
+    kt_end = (int)((long long)all * (split + 1) / n_sp);
+  }
   auto next_active = [&](int jj) __attribute__((always_inline)) {
     if (SPARSE)
       while (jj < kt_end && mask_s[(jj * BC) / MASK_TILE] == 0) ++jj;
@@ -120,8 +135,12 @@ __global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p)
   };
   // Keys past last_key are invisible to every query of this wave; a unit
   // starting at ks needs masking iff ks + 31 > plain_key.
-  const int last_key = CAUSAL ? min(N - 1, q0w + 31) : N - 1;
-  const int plain_key = CAUSAL ? min(N - 1, q0w) : N - 1;
+  // key_last: the last key of this workgroup's run (N - 1 without splits).
+  // The unit after a run's last tile is evaluated (and must come out empty)
+  // like the one past the end of the sequence.
+  const int key_last = min(N, kt_end * BC) - 1;
+  const int last_key = CAUSAL ? min(key_last, q0w + 31) : key_last;
+  const int plain_key = CAUSAL ? min(key_last, q0w) : key_last;
 
   // Copy tile jj of K (or V) into slot `slot` of its ring.  Rows past N read
   // row N - 1: those keys are masked out of every score that is used, and
@@ -147,7 +166,7 @@ __global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p)
   // Q^T fragments (B operand): lane holds query q0w + l32.  Loaded after the
   // first copies are issued; the first use waits for both.
   int jq[NS + 1];  // active tiles n .. n+NS (kt_end past the last one)
-  jq[0] = next_active(0);
+  jq[0] = next_active(kt_begin);
 #pragma unroll
   for (int i = 1; i <= NS; ++i) jq[i] = jq[i - 1] < kt_end ? next_active(jq[i - 1] + 1) : kt_end;
   // Prologue copies, in the order K0 V0 K1 [V1 K2]: iteration n then issues
@@ -251,7 +270,7 @@ __global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p)
   // its probabilities are exactly 0 and its P V adds nothing.
   auto mask_unit = [&](int ks, f32x16& s) __attribute__((always_inline)) {
     if (ks + 31 > plain_key) {
-      const int lim = min(N - 1, CAUSAL ? q0w + l32 : N - 1) - ks - 4 * g;
+      const int lim = min(key_last, CAUSAL ? q0w + l32 : N - 1) - ks - 4 * g;
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (8 * (r >> 2) + (r & 3) > lim) s[r] = -INFINITY;
@@ -351,6 +370,23 @@ __global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p)
   const float lt = half_swap_sum(l_run);
   const float inv = lt > 0.f ? (DROP ? p.drop_scale : 1.0f) / lt : 0.f;
   const int q = q0w + l32;
+  if (n_sp > 1) {
+    // Partial result of this key range, fp32, for the merge kernel; a range
+    // with no visible key leaves O = 0 and lse = -inf (weight 0 there).
+    if (q < N) {
+      const size_t prow = ((size_t)bh * n_sp + split) * N + q;
+      float* orow = p.o_part + prow * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg)
+          *(float4*)(orow + 32 * db + 8 * rg + 4 * g) =
+              make_float4(o[db][4 * rg] * inv, o[db][4 * rg + 1] * inv, o[db][4 * rg + 2] * inv,
+                          o[db][4 * rg + 3] * inv);
+      if (g == 0) p.lse_part[prow] = lt > 0.f ? m_run * p.scale + logf(lt) : -INFINITY;
+    }
+    return;
+  }
   if (q < N) {
     T* orow = (T*)p.o + base + (size_t)q * D;
 #pragma unroll
@@ -505,7 +541,7 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(FwdParams p) {
 
 template <typename T, int D>
 hipError_t launch16(const FwdParams& p, bool causal, bool sparse, hipStream_t st) {
-  dim3 grid(((p.N + 127) / 128) * p.BH), block(256);
+  dim3 grid(((p.N + 127) / 128) * p.BH * (p.n_splits > 1 ? p.n_splits : 1)), block(256);
   const bool drop = p.drop_t8 > 0;
   if (drop) {
     if (causal && sparse) fwd16_kernel<T, D, true, true, true><<<grid, block, 0, st>>>(p);

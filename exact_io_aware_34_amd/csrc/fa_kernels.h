@@ -46,6 +46,14 @@ struct FwdParams {
   // 1 / (1 - drop_t8 / 256).
   uint32_t drop_k0, drop_k1, drop_off, drop_t8;
   float drop_scale;
+  // Split key ranges (16-bit inputs, no dropout): n_splits > 1 cuts every
+  // query tile's key range into n_splits equal runs of tiles, each its own
+  // workgroup, which writes its normalised partial output and logsumexp to
+  // o_part (B*H, n_splits, N, d) and lse_part (B*H, n_splits, N) -- the
+  // decode workspace layout with Nq = N -- for the decode merge kernel.
+  int n_splits;
+  float* o_part;
+  float* lse_part;
 };
 
 struct BwdParams {
@@ -111,6 +119,9 @@ struct DropMaskParams {
 hipError_t launch_forward(FwdParams p, int dtype, int d, bool causal, hipStream_t st);
 hipError_t launch_backward(BwdParams p, int dtype, int d, bool causal, hipStream_t st);
 hipError_t launch_decode(DecParams p, int dtype, int d, bool causal, hipStream_t st);
+// Merge of per-range partial outputs (o_part, lse_part, n_splits, BH, Nq) into
+// o and lse; the decode path's second kernel.
+hipError_t launch_split_merge(DecParams p, int dtype, int d, hipStream_t st);
 hipError_t launch_dropout_mask(DropMaskParams p, hipStream_t st);
 hipError_t launch_fp8(Fp8Params p, int dtype, int d, bool causal, bool prep, bool attend,
                       hipStream_t st);

@@ -8,6 +8,7 @@ library has not been built (there is no other code path).
     from exact_io_aware_34_amd import fa
     o, lse = fa.forward(q, k, v, causal=True)
     dq, dk, dv = fa.backward(q, k, v, o, lse, do, causal=True)
+    o, lse = fa.forward(q, k, v, n_splits=0)          # split key runs for small grids
     o, lse = fa.decode(q_new, k_cache, v_cache)        # Nq <= 16 queries, Nk keys
     o, lse = fa.forward_fp8(q, k, v, signs=signs, causal=True)   # E4M3 operands
 """
@@ -54,6 +55,13 @@ _lib.fa_backward_dropout.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp
 _lib.fa_backward_dropout.restype = _i
 _lib.fa_dropout_mask.argtypes = [_i, _i, _i, _f, _u64, _u32, _vp, _vp]
 _lib.fa_dropout_mask.restype = _i
+_lib.fa_forward_split.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _i, _i, _vp,
+                                  ctypes.c_size_t, _vp]
+_lib.fa_forward_split.restype = _i
+_lib.fa_forward_splits.argtypes = [_i, _i, _i, _i, _i]
+_lib.fa_forward_splits.restype = _i
+_lib.fa_forward_split_workspace_size.argtypes = [_i, _i, _i, _i, _i]
+_lib.fa_forward_split_workspace_size.restype = ctypes.c_size_t
 _lib.fa_status_string.argtypes = [_i]
 _lib.fa_status_string.restype = ctypes.c_char_p
 _lib.fa_abi_version.restype = _i
@@ -116,10 +124,21 @@ def default_scale(d: int) -> float:
     return float(torch.tensor(d ** -0.5, dtype=torch.float32))
 
 
+def forward_splits(B, H, N, d, n_splits=0) -> int:
+    """Number of key runs fa_forward_split uses for this shape (0 on bad input)."""
+    return int(_lib.fa_forward_splits(B, H, N, d, n_splits))
+
+
+def forward_split_workspace_size(B, H, N, d, n_splits=0) -> int:
+    return int(_lib.fa_forward_split_workspace_size(B, H, N, d, n_splits))
+
+
 def forward(q, k, v, causal=False, scale=None, block_mask=None, out=None, lse=None,
-            stream=None, dropout_p=0.0, seed=0, offset=0):
+            stream=None, dropout_p=0.0, seed=0, offset=0, n_splits=1, workspace=None):
     """Exact attention forward: returns (o, lse) with o in q's dtype, lse fp32.
-    dropout_p > 0 drops probabilities with the mask fa_dropout_mask describes."""
+    dropout_p > 0 drops probabilities with the mask fa_dropout_mask describes.
+    n_splits != 1 runs fa_forward_split (0 = the library's choice of key runs)
+    with `workspace` (allocated here when None)."""
     _check_inputs(q, k, v)
     B, H, N, d = q.shape
     scale = default_scale(d) if scale is None else float(scale)
@@ -129,7 +148,17 @@ def forward(q, k, v, causal=False, scale=None, block_mask=None, out=None, lse=No
     _check_inputs(q, o)
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
         raise ValueError("lse must be contiguous float32 (B, H, N)")
-    if dropout_p:
+    if n_splits != 1:
+        if dropout_p:
+            raise ValueError("split key runs are not offered with dropout")
+        ws_bytes = forward_split_workspace_size(B, H, N, d, n_splits)
+        if workspace is None and ws_bytes > 0:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        rc = _lib.fa_forward_split(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                                   scale, int(bool(causal)), _ptr(mask), DTYPE_CODES[q.dtype],
+                                   int(n_splits), _ptr(workspace), nbytes, _stream(stream))
+    elif dropout_p:
         rc = _lib.fa_forward_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                                      scale, int(bool(causal)), _ptr(mask), DTYPE_CODES[q.dtype],
                                      float(dropout_p), int(seed), int(offset), _stream(stream))

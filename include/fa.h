@@ -75,6 +75,43 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int N, int d, float scale, int causal,
                const uint8_t* block_mask, int dtype, void* stream);
 
+/*
+ * Forward pass with split key ranges, for grids too small to fill the GPU
+ * (few heads, few query tiles): the same o and lse as fa_forward.
+ *
+ * Every query tile's visible key tiles (64 keys each) are cut into n runs of
+ * equal tile count, each computed by its own workgroup with the
+ * online-softmax recurrence into a normalised partial output o_s and its
+ * logsumexp lse_s; a second kernel merges them with the incremental-softmax
+ * merge ("Rastreamento Incremental do Softmax", xyznot.com reading guide):
+ * lse = ln sum_s exp(lse_s), o = sum_s exp(lse_s - lse) o_s.  A run with no
+ * visible key has lse_s = -inf and weight 0.
+ *
+ * n_splits = 0 lets the library choose (fa_forward_splits()): one run unless
+ * the plain grid (B*H*ceil(N/128) workgroups) is smaller than one round of
+ * the GPU (768 workgroups at d = 64, 512 at d = 128), then enough runs for
+ * one round, with at least ten 64-key tiles per run.  An explicit n_splits is
+ * capped at ceil(N / 64) and at 64.  With one run this is fa_forward and no
+ * workspace is used.  `workspace` (at least
+ * fa_forward_split_workspace_size() bytes, 256-byte aligned, caller-owned,
+ * contents ignored on entry) holds the partial results, in this order, each
+ * region padded to 256 bytes: o_part (B*H, n, N, d) fp32, lse_part (B*H, n, N)
+ * fp32.  Supported: dtype FA_F16 and FA_BF16 (FA_F32: n_splits = 0 runs
+ * fa_forward, n_splits > 1 -> FA_ERR_UNSUPPORTED); B*H*n*N < 2^31, else
+ * FA_ERR_UNSUPPORTED; n_splits < 0 -> FA_ERR_INVALID_ARG.
+ */
+int fa_forward_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int N, int d, float scale, int causal,
+                     const uint8_t* block_mask, int dtype, int n_splits, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* Number of key runs fa_forward_split uses for this shape (0 on bad input). */
+int fa_forward_splits(int B, int H, int N, int d, int n_splits);
+
+/* Bytes of workspace fa_forward_split needs (0 when it uses one run or on bad
+ * input). */
+size_t fa_forward_split_workspace_size(int B, int H, int N, int d, int n_splits);
+
 /* Bytes of device workspace fa_backward needs for this shape (0 on bad input):
  * two fp32 values per (b, h, row), each array padded to 256 bytes. */
 size_t fa_backward_workspace_size(int B, int H, int N, int d);

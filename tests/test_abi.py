@@ -41,6 +41,11 @@ def lib():
     L.fa_backward_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i,
                                       f, u64, u32, vp, ctypes.c_size_t, vp]
     L.fa_dropout_mask.argtypes = [i, i, i, f, u64, u32, vp, vp]
+    L.fa_forward_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, i, vp,
+                                   ctypes.c_size_t, vp]
+    L.fa_forward_splits.argtypes = [i] * 5
+    L.fa_forward_split_workspace_size.argtypes = [i] * 5
+    L.fa_forward_split_workspace_size.restype = ctypes.c_size_t
     return L
 
 
@@ -55,7 +60,8 @@ def test_header_declares_the_boundary():
         "fa_abi_version", "fa_backward", "fa_backward_workspace_size", "fa_decode",
         "fa_decode_splits", "fa_decode_workspace_size", "fa_dropout_mask", "fa_forward",
         "fa_forward_dropout", "fa_forward_fp8", "fa_forward_fp8_workspace_size", "fa_fp8_prepare",
-        "fa_backward_dropout", "fa_status_string"])
+        "fa_backward_dropout", "fa_status_string", "fa_forward_split", "fa_forward_splits",
+        "fa_forward_split_workspace_size"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -222,3 +228,59 @@ def test_dropout_validation(lib):
     assert lib.fa_dropout_mask(1, 1, 10, 0.5, 1, 0, None, None) == -1
     assert lib.fa_dropout_mask(1, 1, 10, 1.0, 1, 0, FAKE, None) == -1
     assert lib.fa_dropout_mask(1, 1, 70000, 0.5, 1, 0, FAKE, None) == -2
+
+
+def test_forward_split_choice(lib):
+    S = lib.fa_forward_splits
+    # Automatic: one run once the plain grid fills a round (768 workgroups at
+    # d = 64, 512 at d = 128).
+    assert S(4, 12, 8192, 64, 0) == 1          # 3072 query tiles
+    assert S(1, 6, 16384, 64, 0) == 1          # 768
+    assert S(1, 4, 16384, 128, 0) == 1         # 512
+    # Smaller grids: one round of (query tile, run) workgroups, >= 10 key tiles per run.
+    assert S(1, 4, 16384, 64, 0) == 2          # 512 tiles -> ceil(768 / 512)
+    assert S(1, 1, 4096, 64, 0) == 6           # 32 tiles -> 24 wanted, 64 key tiles / 10
+    assert S(1, 1, 16384, 64, 0) == 6          # 128 tiles -> ceil(768 / 128)
+    assert S(1, 2, 8192, 128, 0) == 4          # 128 tiles -> ceil(512 / 128)
+    assert S(1, 2, 4096, 128, 0) == 6          # 64 tiles -> 8 wanted, 64 key tiles / 10
+    assert S(1, 1, 256, 64, 0) == 1            # 4 key tiles
+    assert S(1, 1, 1000, 64, 0) == 1           # 16 key tiles: one run of >= 10
+    # Explicit counts are capped at the key tiles and at 64.
+    assert S(1, 1, 300, 64, 9) == 5
+    assert S(1, 1, 1 << 16, 64, 100) == 64
+    assert S(1, 1, 4096, 64, 3) == 3
+    # Bad input
+    assert S(0, 1, 10, 64, 0) == 0
+    assert S(1, 1, 10, 96, 0) == 0
+    assert S(1, 1, 10, 64, -1) == 0
+
+
+def test_forward_split_workspace_size(lib):
+    W = lib.fa_forward_split_workspace_size
+    assert W(4, 12, 8192, 64, 0) == 0          # one run
+    assert W(1, 1, 300, 64, 1) == 0
+    # 6 runs of 4096 rows x 64 fp32, then 6 x 4096 fp32
+    assert W(1, 1, 4096, 64, 0) == 6 * 4096 * 64 * 4 + 6 * 4096 * 4
+    assert W(1, 2, 300, 128, 3) == 2 * 3 * 300 * 128 * 4 + (-(-2 * 3 * 300 * 4 // 256)) * 256
+
+
+def fsplit(lib, q=FAKE, lse=FAKE, B=1, H=1, N=4096, d=64, scale=0.125, dtype=2, n=4, ws=FAKE,
+           ws_bytes=1 << 30):
+    return lib.fa_forward_split(q, FAKE, FAKE, FAKE, lse, B, H, N, d, scale, 0, None, dtype, n,
+                                ws, ws_bytes, None)
+
+
+def test_forward_split_validation(lib):
+    assert fsplit(lib, n=-1) == -1
+    assert fsplit(lib, q=None) == -1
+    assert fsplit(lib, q=MISALIGNED) == -1
+    assert fsplit(lib, lse=None) == -1
+    assert fsplit(lib, B=0) == -1
+    assert fsplit(lib, dtype=9) == -1
+    assert fsplit(lib, scale=float("inf")) == -1
+    assert fsplit(lib, d=80) == -2
+    assert fsplit(lib, dtype=0) == -2          # fp32 with explicit runs
+    assert fsplit(lib, ws=None) == -3
+    assert fsplit(lib, ws=MISALIGNED) == -3
+    need = lib.fa_forward_split_workspace_size(1, 1, 4096, 64, 4)
+    assert need > 0 and fsplit(lib, ws_bytes=need - 1) == -3
