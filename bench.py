@@ -23,8 +23,8 @@ The same step with fused dropout (fa_forward_dropout + fa_backward_dropout,
 probability 0.1 by default, a fixed seed) is timed after the plain steps and
 reported in the `dropout` object, with the same FLOP count.
 
-On workloads whose forward grid is too small to fill the GPU (16-bit inputs,
-fewer than 512 query tiles in all), the `split_forward` object times
+On workloads whose forward grid is too small to fill the GPU (fewer query
+tiles in all than one round of workgroups), the `split_forward` object times
 fa_forward_split with the library's number of key runs.
 
 The FP8 forward (fa_forward_fp8: rotation + block quantisation, then
@@ -325,7 +325,7 @@ def bench_split(fa, w, tensors, mask, steps, warmup, fwd_ms):
             "ms_median_min": [round(statistics.median(ms), 4), round(min(ms), 4)],
             "tflops": round(tf, 2), "frac_peak": round(tf / peak, 4),
             "vs_plain_forward": round(fwd_ms / mean, 3),
-            "kernels": "fwd16 over key runs + dec_combine merge"}
+            "kernels": "forward kernel over key runs + dec_combine merge"}
 
 
 def bench_fp8(fa, w, inputs, tensors, mask, steps, warmup, cpu_heads, with_cpu):
@@ -483,7 +483,7 @@ def main():
             "bwd": round(mean(d_bwd) / mean(bwd_ms) * kept, 4) if w.backward else None,
             "dense_fwd_ms": round(mean(d_fwd), 4),
             "dense_bwd_ms": round(mean(d_bwd), 4) if w.backward else None}
-    if w.dtype in ("bf16", "f16") and fa.forward_splits(B, H, N, d, 0) > 1:
+    if fa.forward_splits(B, H, N, d, 0) > 1:
         out["split_forward"] = bench_split(fa, w, tensors, mask, args.steps, args.warmup,
                                            mean(fwd_ms))
     if not args.no_dropout and w.dtype in ("bf16", "f16") and w.backward:

@@ -260,13 +260,12 @@ int fa_forward_split(const void* q, const void* k, const void* v, void* o, float
   const int rc = check_common(B, H, N, d, scale, dtype);
   if (rc != FA_OK) return rc;
   const int n = forward_split_count(B, H, N, d, n_splits);
-  if (n <= 1 || (dtype == FA_F32 && n_splits == 0))
+  if (n <= 1)
     return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, dtype, 0.f, 0, 0,
                         stream);
   if (!tensor_ptr_ok(q) || !tensor_ptr_ok(k) || !tensor_ptr_ok(v) || !tensor_ptr_ok(o))
     return FA_ERR_INVALID_ARG;
   if (lse == nullptr || !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
-  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   if (block_mask != nullptr && (N + fa::MASK_TILE - 1) / fa::MASK_TILE > fa::FWD_MAX_MASK_TILES)
     return FA_ERR_UNSUPPORTED;
   // Partial rows and the split grid are indexed with int in the kernels.

@@ -334,6 +334,9 @@ hipError_t launch_split_merge(DecParams p, int dtype, int d, hipStream_t st) {
   if (dtype == DT_BF16) {
     if (d == 64) hipLaunchKernelGGL((dec_combine_kernel<__bf16, 64>), grid, dim3(256), 0, st, p);
     else hipLaunchKernelGGL((dec_combine_kernel<__bf16, 128>), grid, dim3(256), 0, st, p);
+  } else if (dtype == DT_F32) {
+    if (d == 64) hipLaunchKernelGGL((dec_combine_kernel<float, 64>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((dec_combine_kernel<float, 128>), grid, dim3(256), 0, st, p);
   } else {
     if (d == 64) hipLaunchKernelGGL((dec_combine_kernel<_Float16, 64>), grid, dim3(256), 0, st, p);
     else hipLaunchKernelGGL((dec_combine_kernel<_Float16, 128>), grid, dim3(256), 0, st, p);

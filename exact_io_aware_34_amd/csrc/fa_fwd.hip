@@ -415,7 +415,15 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(FwdParams p) {
   const int g = lane >> 5, l32 = lane & 31;
   const int N = p.N;
   const int total = p.n_qtiles * p.BH;
-  const int lid = xcd_remap(blockIdx.x, total);
+  // Split key runs as in the 16-bit kernel: consecutive workgroups share a
+  // query tile, one run of key tiles each.
+  const int n_sp = p.n_splits;
+  int bid = blockIdx.x, split = 0;
+  if (n_sp > 1) {
+    split = bid % n_sp;
+    bid /= n_sp;
+  }
+  const int lid = xcd_remap(bid, total);
   const int bh = lid / p.n_qtiles;
   const int ir = lid - bh * p.n_qtiles;
   const int qt = CAUSAL ? (p.n_qtiles - 1 - ir) : ir;
@@ -432,6 +440,12 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(FwdParams p) {
 
   int kt_end = (N + BC - 1) / BC;
   if (CAUSAL) kt_end = min(kt_end, (min(N, (qt + 1) * BR) + BC - 1) / BC);
+  int kt_begin = 0;
+  if (n_sp > 1) {
+    const int all = kt_end;
+    kt_begin = (int)((long long)all * split / n_sp);
+    kt_end = (int)((long long)all * (split + 1) / n_sp);
+  }
   const uint8_t* mrow = SPARSE ? p.mask + (size_t)qt * p.mask_tiles : nullptr;
   auto next_active = [&](int j) __attribute__((always_inline)) {
     if (SPARSE)
@@ -469,7 +483,7 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(FwdParams p) {
   float m_run = -1e30f, l_run = 0.f;
   const float c = p.scale_log2e;
 
-  int j = next_active(0);
+  int j = next_active(kt_begin);
   if (j < kt_end) {
     gload(j);
     lstore(0);
@@ -526,7 +540,10 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(FwdParams p) {
   const float lt = half_swap_sum(l_run);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   if (my_q < N) {
-    float* orow = (float*)p.o + base + (size_t)my_q * D;
+    // With runs: this run's normalised partial output and logsumexp.
+    const size_t prow = ((size_t)bh * n_sp + split) * N + my_q;
+    float* orow = n_sp > 1 ? p.o_part + prow * D : (float*)p.o + base + (size_t)my_q * D;
+    float* lrow = n_sp > 1 ? p.lse_part + prow : p.lse + (size_t)bh * N + my_q;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -535,7 +552,7 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(FwdParams p) {
                                o[db][4 * rg + 2] * inv, o[db][4 * rg + 3] * inv);
         *(float4*)(orow + 32 * db + 8 * rg + 4 * g) = h;
       }
-    if (g == 0) p.lse[(size_t)bh * N + my_q] = lt > 0.f ? m_run * p.scale + logf(lt) : -INFINITY;
+    if (g == 0) *lrow = lt > 0.f ? m_run * p.scale + logf(lt) : -INFINITY;
   }
 }
 
@@ -557,7 +574,7 @@ hipError_t launch16(const FwdParams& p, bool causal, bool sparse, hipStream_t st
 
 template <int D>
 hipError_t launch32(const FwdParams& p, bool causal, bool sparse, hipStream_t st) {
-  dim3 grid(p.n_qtiles * p.BH), block(256);
+  dim3 grid(p.n_qtiles * p.BH * (p.n_splits > 1 ? p.n_splits : 1)), block(256);
   if (causal && sparse) fwd32_kernel<D, true, true><<<grid, block, 0, st>>>(p);
   else if (causal) fwd32_kernel<D, true, false><<<grid, block, 0, st>>>(p);
   else if (sparse) fwd32_kernel<D, false, true><<<grid, block, 0, st>>>(p);

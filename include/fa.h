@@ -96,9 +96,8 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
  * fa_forward_split_workspace_size() bytes, 256-byte aligned, caller-owned,
  * contents ignored on entry) holds the partial results, in this order, each
  * region padded to 256 bytes: o_part (B*H, n, N, d) fp32, lse_part (B*H, n, N)
- * fp32.  Supported: dtype FA_F16 and FA_BF16 (FA_F32: n_splits = 0 runs
- * fa_forward, n_splits > 1 -> FA_ERR_UNSUPPORTED); B*H*n*N < 2^31, else
- * FA_ERR_UNSUPPORTED; n_splits < 0 -> FA_ERR_INVALID_ARG.
+ * fp32.  Supported: every dtype and head dimension fa_forward supports;
+ * B*H*n*N < 2^31, else FA_ERR_UNSUPPORTED; n_splits < 0 -> FA_ERR_INVALID_ARG.
  */
 int fa_forward_split(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int H, int N, int d, float scale, int causal,

@@ -279,7 +279,6 @@ def test_forward_split_validation(lib):
     assert fsplit(lib, dtype=9) == -1
     assert fsplit(lib, scale=float("inf")) == -1
     assert fsplit(lib, d=80) == -2
-    assert fsplit(lib, dtype=0) == -2          # fp32 with explicit runs
     assert fsplit(lib, ws=None) == -3
     assert fsplit(lib, ws=MISALIGNED) == -3
     need = lib.fa_forward_split_workspace_size(1, 1, 4096, 64, 4)

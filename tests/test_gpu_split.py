@@ -5,7 +5,7 @@ The split forward must give what fa_forward gives: the same attention, here
 reached by per-run online softmax plus the logsumexp merge.  Cases cover
 automatic and explicit run counts, runs left empty (more runs than a short
 causal row has key tiles), ragged N, block-sparse masks whose runs hold no
-kept tile, both head dimensions and both 16-bit types.
+kept tile, both head dimensions and all three input types.
 """
 
 import pytest
@@ -47,6 +47,10 @@ CASES = [
     (1, 1, 900, 128, "f16", True, False, 4),
     (1, 1, 1000, 128, "bf16", True, True, 6),
     (1, 1, 64, 64, "bf16", True, False, 2),      # one key tile: one run
+    (1, 1, 4096, 64, "f32", False, False, 0),
+    (1, 2, 700, 64, "f32", True, False, 4),
+    (1, 1, 1000, 128, "f32", True, True, 5),
+    (1, 1, 333, 128, "f32", False, False, 3),
 ]
 
 
@@ -79,10 +83,11 @@ def test_split_counts_agree(fa):
         assert_close(f"lse n={n}", f64(ln), f64(l1), LSE_TOL)
 
 
-def test_split_named_small_workload(fa):
-    """The single-head bf16 workload (N = 4096, 32 query tiles) in the
-    configuration the benchmark times for it (library-chosen run count)."""
-    w = W.make("dense_n4096_d64_bf16")
+@pytest.mark.parametrize("name", ["dense_n4096_d64_bf16", "dense_n4096_d64_f32"])
+def test_split_named_small_workload(fa, name):
+    """The single-head N = 4096 workloads (32 query tiles) in the
+    configuration the benchmark times for them (library-chosen run count)."""
+    w = W.make(name)
     wl = w["workload"]
     assert fa.forward_splits(wl.B, wl.H, wl.N, wl.d, 0) > 1
     o, lse = run_split(fa, w["q"], w["k"], w["v"], w["scale"], w["causal"], w["mask"], 0)
