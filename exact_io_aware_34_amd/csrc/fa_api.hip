@@ -215,11 +215,11 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
 // Key runs of the split forward.  n_splits = 0 picks a count for grids
 // smaller than one full round of workgroups (768 at d = 64: three per CU;
 // 512 at d = 128: two): enough (query tile, run) workgroups for one round,
-// with runs of at least ten 64-key tiles.  A sweep of the count on one to
-// four heads of N = 4096..16384 found the fastest counts within 7 % of this
-// choice (runs shorter than ~10 tiles spend most of their time filling and
-// draining the copy pipeline).  An explicit count is capped at the number of
-// 64-key tiles.
+// with runs of at least ten 64-key tiles.  In a sweep of the count (1..32)
+// on five shapes (one to four heads, N = 4096..16384, d = 64 and 128, causal
+// and not) this choice was the fastest count on every one; runs shorter than
+// ~10 tiles spend most of their time filling and draining the copy
+// pipeline.  An explicit count is capped at the number of 64-key tiles.
 int forward_split_count(int B, int H, int N, int d, int n_splits) {
   if (B < 1 || H < 1 || N < 1 || n_splits < 0 || (d != 64 && d != 128)) return 0;
   const long long n_kt = (N + 63) / 64;
