@@ -27,8 +27,9 @@ constexpr int dec_waves(int d) { return d == 64 ? 2 : 1; }
 constexpr int DEC_MAX_NQ = 16;  // queries per head the decode kernel holds (one MFMA column block)
 constexpr int DEC_SPLIT_ALIGN = 128;  // key-range lengths are multiples of 4 waves x 32 keys
 // FP8 forward: waves per SIMD (three-slot rings of 64-key E4M3 K and V^T
-// tiles: 24 KiB at d = 64, 48 KiB at d = 128).
-constexpr int fwd8_waves(int d) { return d == 64 ? 3 : 2; }
+// tiles: 24 KiB at d = 64, 48 KiB at d = 128).  d = 64 fits four waves in
+// 128 VGPRs with two values spilled around (not inside) the key loop.
+constexpr int fwd8_waves(int d) { return d == 64 ? 4 : 2; }
 constexpr int FWD_MAX_MASK_TILES = 2048;  // block-mask columns the forward caches (N <= 262144)
 
 struct FwdParams {
