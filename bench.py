@@ -400,8 +400,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards over independent (batch, head) pairs; see DESIGN.md)",
-              file=sys.stderr)
+              "(the path would shard over independent (batch, head) pairs with no "
+              "communication; that sharding is not built)", file=sys.stderr)
         sys.exit(2)
     import torch
 
