@@ -57,7 +57,7 @@ typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
 typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, B/H/N < 1, bad dtype, scale not finite > 0 */
-  FA_ERR_UNSUPPORTED = -2, /* valid request this build does not implement (e.g. d not 64/128) */
+  FA_ERR_UNSUPPORTED = -2, /* valid request the library does not implement (e.g. d not 64/128) */
   FA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than its *_workspace_size() */
   FA_ERR_HIP = -4          /* the HIP runtime reported an error at launch */
 } fa_status;

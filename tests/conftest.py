@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests are skipped (not failed) where no GPU is visible, so a plain
-    # `pytest tests/` on a CPU machine stays green; `-m gpu` on the GPU machine runs them.
+    # `pytest tests/` on a machine without a GPU stays green; `-m gpu` on an MI355X runs them.
     try:
         import torch
         has_gpu = torch.cuda.is_available()
