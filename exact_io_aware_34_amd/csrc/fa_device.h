@@ -332,6 +332,21 @@ __device__ __forceinline__ bool drop_keep(const uint32_t (&c)[4], int r, uint32_
   return ((c[r >> 2] >> (8 * (r & 3))) & 0xFFu) >= t8;
 }
 
+// The keep decisions of the four bytes of w (byte i kept iff byte_i >= t8)
+// as masks for two packed 16-bit pairs: lo = bytes 0, 1 -> halves 0xFFFF or
+// 0, hi = bytes 2, 3.  Byte-parallel compare: bit 7 of byte i of
+// ((w & 0x7F..) | 0x80..) - (t8 & 0x7F) * 0x01.. is (byte_i & 0x7F) >= (t8 & 0x7F)
+// (no borrow crosses a byte); combined with the byte's own top bit it gives
+// byte_i >= t8.  v_perm's sign selectors (8..11: bit 7 of bytes 1, 3, 5, 7
+// of {S0, S1}) spread the four flags into 16-bit halves.
+__device__ __forceinline__ void drop_masks16(uint32_t w, uint32_t t8, uint32_t& lo, uint32_t& hi) {
+  const uint32_t d = ((w & 0x7F7F7F7Fu) | 0x80808080u) - (t8 & 0x7Fu) * 0x01010101u;
+  const uint32_t ge = (t8 & 0x80u) ? (w & d) : (w | d);  // bit 8i+7: byte i kept
+  const uint32_t ge8 = ge << 8;                          // bit 8i+15: byte i kept
+  lo = __builtin_amdgcn_perm(ge8, ge, 0x08080A0Au);      // [b0, b0, b1, b1]
+  hi = __builtin_amdgcn_perm(ge8, ge, 0x09090B0Bu);      // [b2, b2, b3, b3]
+}
+
 // Workgroup index -> logical tile index.  The hardware hands consecutive
 // workgroup ids to the 8 XCDs round robin; this mapping gives each XCD a
 // contiguous range of logical ids so tiles of one head share that XCD's L2.

@@ -228,15 +228,19 @@ __global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 8 * h + 2 * e;
-        float e0 = fast_exp2(fmaf(s[r], c, -mc));
-        float e1 = fast_exp2(fmaf(s[r + 1], c, -mc));
+        const float e0 = fast_exp2(fmaf(s[r], c, -mc));
+        const float e1 = fast_exp2(fmaf(s[r + 1], c, -mc));
         ls0 = r == 0 ? e0 : ls0 + e0;
         ls1 = r == 0 ? e1 : ls1 + e1;
-        if constexpr (DROP) {
-          e0 = drop_keep(dw, r, p.drop_t8) ? e0 : 0.f;
-          e1 = drop_keep(dw, r + 1, p.drop_t8) ? e1 : 0.f;
-        }
         w[e] = pack2<T>(e0, e1);
+      }
+      if constexpr (DROP) {
+        // Dropped probabilities become +0 in the packed P V operand.
+        uint32_t m[4];
+        drop_masks16(dw[2 * h], p.drop_t8, m[0], m[1]);
+        drop_masks16(dw[2 * h + 1], p.drop_t8, m[2], m[3]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] &= m[e];
       }
       pu[h] = __builtin_bit_cast(VT, w);
     }
