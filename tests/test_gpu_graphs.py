@@ -3,10 +3,10 @@
 Every call only launches kernels on the caller's stream (no allocation, no
 memset, no synchronisation), so a sequence of calls with caller-owned
 buffers can be captured once and replayed.  The test captures a forward +
-backward step and a split-KV decode into one graph, then replays it several
-times with new inputs copied into the captured buffers by ordinary eager work
-between the replays, and checks every replay bit for bit against the same
-calls made eagerly on separate buffers.
+backward step, a split-KV decode and a split-key-run forward into one graph,
+then replays it several times with new inputs copied into the captured
+buffers by ordinary eager work between the replays, and checks every replay
+bit for bit against the same calls made eagerly on separate buffers.
 """
 
 import pytest
@@ -35,11 +35,16 @@ def test_graph_replays_match_eager(fa):
     xo = torch.empty_like(xq)
     xlse = torch.empty(B, H, Nq, device="cuda")
     xws = torch.empty(fa.decode_workspace_size(B, H, Nq, Nk, d, 3), dtype=torch.uint8, device="cuda")
+    so = torch.empty_like(q)
+    slse = torch.empty(B, H, N, device="cuda")
+    sws = torch.empty(fa.forward_split_workspace_size(B, H, N, d, 4), dtype=torch.uint8,
+                      device="cuda")
 
     def step():
         fa.forward(q, k, v, causal=True, out=o, lse=lse)
         fa.backward(q, k, v, o, lse, do, causal=True, workspace=ws, grads=grads)
         fa.decode(xq, xk, xv, causal=True, n_splits=3, out=xo, lse=xlse, workspace=xws)
+        fa.forward(q, k, v, causal=True, out=so, lse=slse, n_splits=4, workspace=sws)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -59,8 +64,10 @@ def test_graph_replays_match_eager(fa):
         eo, el = fa.forward(nq, nk, nv, causal=True)
         eg = fa.backward(nq, nk, nv, eo, el, ndo, causal=True)
         exo, exl = fa.decode(mq, mk, mv, causal=True, n_splits=3)
+        eso, esl = fa.forward(nq, nk, nv, causal=True, n_splits=4)
         torch.cuda.synchronize()
         checks = [("o", o, eo), ("lse", lse, el), ("dq", grads[0], eg[0]), ("dk", grads[1], eg[1]),
-                  ("dv", grads[2], eg[2]), ("decode o", xo, exo), ("decode lse", xlse, exl)]
+                  ("dv", grads[2], eg[2]), ("decode o", xo, exo), ("decode lse", xlse, exl),
+                  ("split o", so, eso), ("split lse", slse, esl)]
         for name, got, want in checks:
             assert torch.equal(got, want), f"replay with seed {seed}: {name} differs from eager"
