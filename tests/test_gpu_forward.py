@@ -116,3 +116,29 @@ def test_forward_named_large_workloads(fa, name):
         assert_close(f"o[{b},{h}] rows", f64(o[b, h][rows]), ro, tol)
         assert_close(f"lse[{b},{h}] rows", f64(lse[b, h][rows]), rl, LSE_TOL)
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+WIDE = [
+    # B, H, N, d, dtype, causal: many heads of short sequences (grids of
+    # 1024-4096 workgroups, each a short key loop)
+    (8, 64, 300, 64, "bf16", True),
+    (8, 64, 300, 64, "f16", False),
+    (4, 64, 777, 64, "bf16", False),
+    (2, 128, 513, 64, "f16", True),
+    (1, 512, 64, 64, "bf16", True),
+    (1, 600, 1, 64, "bf16", False),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype,causal", WIDE)
+def test_forward_many_heads(fa, B, H, N, d, dtype, causal):
+    """Many heads of short sequences; a sample of heads is checked in full."""
+    q, k, v, _ = W.draw_qkvdo(B, H, N, d, dtype, seed=B * H + N)
+    scale = W.scale_for(d)
+    o, lse = run_fwd(fa, q, k, v, scale, causal, None)
+    heads = [(0, 0), (B - 1, H - 1), (B // 2, H // 3), (0, H - 1)]
+    tol = TOL[DT[dtype]]
+    for (b, h), (ro, rl) in zip(heads, oracle_forward_heads(q, k, v, scale, causal, None, heads)):
+        assert_close(f"o[{b},{h}]", f64(o[b, h]), ro, tol)
+        assert_close(f"lse[{b},{h}]", f64(lse[b, h]), rl, LSE_TOL)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
