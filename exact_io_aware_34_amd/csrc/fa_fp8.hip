@@ -88,7 +88,8 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8Params p) {
   using VT = typename V8<T>::t;
   constexpr int EPT = D / 4;        // elements per lane (four lanes per row)
   __shared__ float red[4];
-  __shared__ __attribute__((aligned(16))) uint8_t vtile[64 * D];
+  constexpr int RSB = D + 4;        // V code tile row stride in LDS (bytes)
+  __shared__ __attribute__((aligned(16))) uint8_t vtile[64 * RSB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int z = blockIdx.y;         // 0 = Q, 1 = K, 2 = V
@@ -173,27 +174,32 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8Params p) {
       *(i32x4*)(dst + 16 * i) = i32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
     return;
   }
-  // V: transpose the block through LDS into [d][64 positions].
+  // V: transpose the block through LDS into [d][64 positions].  Rows are
+  // padded to D + 4 bytes so that the column reads below hit distinct banks.
+  // Each thread moves 4 x 4 byte blocks: the four keys of positions
+  // 4j .. 4j+3 (consecutive keys) at columns 4dq .. 4dq+3, read as four
+  // dwords and transposed with byte permutes into one dword per column.
 #pragma unroll
-  for (int i = 0; i < EPT / 4; ++i) *(int*)(vtile + row * D + qd * EPT + 4 * i) = w[i];
+  for (int i = 0; i < EPT / 4; ++i) *(int*)(vtile + row * RSB + qd * EPT + 4 * i) = w[i];
   __syncthreads();
-  constexpr int OB = D * 64 / 256;  // output bytes per thread
-  uint8_t* dst = p.v8t + ((size_t)bh * nt + t) * (64 * D) + tid * OB;
+  uint8_t* dst0 = p.v8t + ((size_t)bh * nt + t) * (64 * D);
 #pragma unroll
-  for (int i = 0; i < OB / 16; ++i) {
-    int ov[4];
+  for (int kq = 0; kq < D / 64; ++kq) {
+    const int P = tid + 256 * kq, j = P & 15, dq = P >> 4;
+    const int k0 = vt_key(4 * j);
+    uint32_t r[4];
 #pragma unroll
-    for (int dw = 0; dw < 4; ++dw) {
-      unsigned acc = 0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int o = tid * OB + 16 * i + 4 * dw + b;
-        const int d = o >> 6, pos = o & 63;
-        acc |= (unsigned)vtile[vt_key(pos) * D + d] << (8 * b);
-      }
-      ov[dw] = (int)acc;
-    }
-    *(i32x4*)(dst + 16 * i) = i32x4{ov[0], ov[1], ov[2], ov[3]};
+    for (int i = 0; i < 4; ++i) r[i] = *(const uint32_t*)(vtile + (k0 + i) * RSB + 4 * dq);
+    // perm(S0, S1, sel): bytes 0-3 of S1, 4-7 of S0.
+    const uint32_t a01l = __builtin_amdgcn_perm(r[1], r[0], 0x05010400u);  // r0b0 r1b0 r0b1 r1b1
+    const uint32_t a01h = __builtin_amdgcn_perm(r[1], r[0], 0x07030602u);  // r0b2 r1b2 r0b3 r1b3
+    const uint32_t a23l = __builtin_amdgcn_perm(r[3], r[2], 0x05010400u);
+    const uint32_t a23h = __builtin_amdgcn_perm(r[3], r[2], 0x07030602u);
+    uint8_t* o = dst0 + (size_t)(4 * dq) * 64 + 4 * j;
+    *(uint32_t*)(o) = __builtin_amdgcn_perm(a23l, a01l, 0x05040100u);        // column 4dq
+    *(uint32_t*)(o + 64) = __builtin_amdgcn_perm(a23l, a01l, 0x07060302u);   // 4dq + 1
+    *(uint32_t*)(o + 128) = __builtin_amdgcn_perm(a23h, a01h, 0x05040100u);  // 4dq + 2
+    *(uint32_t*)(o + 192) = __builtin_amdgcn_perm(a23h, a01h, 0x07060302u);  // 4dq + 3
   }
 }
 
