@@ -278,13 +278,16 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdPara
         nd[3] = d4.w;
       }
       float pv[4], dsv[4];
+      uint32_t km[4];  // keep masks of elements 4 rg .. 4 rg + 3 (dropout only)
+      if constexpr (DROP) drop_masks32(dwk[rg], p.drop_t8, km);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         pv[e] = fast_exp2(fmaf(s[4 * rg + e], c, -lv[e]));
         if constexpr (DROP) {
-          const bool kp = drop_keep(dwk, 4 * rg + e, p.drop_t8);
-          dsv[e] = pv[e] * ((kp ? dp[4 * rg + e] * p.drop_scale : 0.f) + nd[e]);
-          pv[e] = kp ? pv[e] : 0.f;
+          // Selections as ANDs with the keep masks (a ternary here was
+          // compiled to a branch per element).
+          dsv[e] = pv[e] * (and_bits(dp[4 * rg + e] * p.drop_scale, km[e]) + nd[e]);
+          pv[e] = and_bits(pv[e], km[e]);
         } else {
           dsv[e] = pv[e] * dp[4 * rg + e];
         }

@@ -347,6 +347,22 @@ __device__ __forceinline__ void drop_masks16(uint32_t w, uint32_t t8, uint32_t& 
   hi = __builtin_amdgcn_perm(ge8, ge, 0x09090B0Bu);      // [b2, b2, b3, b3]
 }
 
+// The same decisions as four 32-bit masks (0xFFFFFFFF where byte i is
+// kept), for selecting fp32 values with an AND: no compare, no branch.
+__device__ __forceinline__ void drop_masks32(uint32_t w, uint32_t t8, uint32_t (&m)[4]) {
+  const uint32_t d = ((w & 0x7F7F7F7Fu) | 0x80808080u) - (t8 & 0x7Fu) * 0x01010101u;
+  const uint32_t ge = (t8 & 0x80u) ? (w & d) : (w | d);
+  const uint32_t ge8 = ge << 8;
+  m[0] = __builtin_amdgcn_perm(ge8, ge, 0x0A0A0A0Au);
+  m[1] = __builtin_amdgcn_perm(ge8, ge, 0x08080808u);
+  m[2] = __builtin_amdgcn_perm(ge8, ge, 0x0B0B0B0Bu);
+  m[3] = __builtin_amdgcn_perm(ge8, ge, 0x09090909u);
+}
+
+__device__ __forceinline__ float and_bits(float x, uint32_t m) {
+  return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) & m);
+}
+
 // Workgroup index -> logical tile index.  The hardware hands consecutive
 // workgroup ids to the 8 XCDs round robin; this mapping gives each XCD a
 // contiguous range of logical ids so tiles of one head share that XCD's L2.
