@@ -308,10 +308,13 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdPara
   auto mask_unit = [&](int qa, f32x16& s) __attribute__((always_inline)) {
     if ((CAUSAL && qa <= kw0) || qa + 32 > N) {
       const int first = CAUSAL ? my_k : 0;  // first visible query
+      // Visible iff first <= q < N: one unsigned compare and a select per
+      // element (the two-sided test was compiled to branches).
+      const unsigned span = (unsigned)(N - first);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int q = qa + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (q < first || q >= N) s[r] = -INFINITY;
+        s[r] = (unsigned)(q - first) < span ? s[r] : -INFINITY;
       }
     }
   };
