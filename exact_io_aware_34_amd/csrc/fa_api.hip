@@ -149,7 +149,7 @@ int fp8_setup(fa::Fp8Params& p, const void* q, const void* k, const void* v, int
 
 extern "C" {
 
-int fa_abi_version(void) { return 1; }
+int fa_abi_version(void) { return 2; }
 
 const char* fa_status_string(int status) {
   switch (status) {

@@ -581,7 +581,7 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dq_u_kernel(BwdParams
       const int lim = min(N - 1, CAUSAL ? my_q : N - 1) - ks - 4 * g;
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (8 * (r >> 2) + (r & 3) > lim) s[r] = -INFINITY;
+        s[r] = 8 * (r >> 2) + (r & 3) > lim ? -INFINITY : s[r];
     }
   };
   auto block = [&](int kslc, int vslc, int gslc, int h, int ks, f32x16& s_cur, f32x16& dp_cur,

@@ -277,7 +277,7 @@ __global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p)
       const int lim = min(key_last, CAUSAL ? q0w + l32 : N - 1) - ks - 4 * g;
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (8 * (r >> 2) + (r & 3) > lim) s[r] = -INFINITY;
+        s[r] = 8 * (r >> 2) + (r & 3) > lim ? -INFINITY : s[r];
     }
   };
   // One block: matrix work of the neighbouring units (scores of the next,

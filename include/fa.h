@@ -274,7 +274,7 @@ size_t fa_forward_fp8_workspace_size(int B, int H, int N, int d);
 /* Static, human-readable text for a status code. */
 const char* fa_status_string(int status);
 
-/* Library ABI version (this header: 1). */
+/* Library ABI version (this header: 2; 2 added fa_forward_split*). */
 int fa_abi_version(void);
 
 #ifdef __cplusplus
