@@ -5,7 +5,8 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-
                 [--no-dropout] [--dropout-p P]
 
 A step is one forward pass and one backward pass (every kernel of the path:
-forward, backward preprocess, backward main) over the workload's synthetic
+forward, then the backward's dQ kernel -- which also computes each row's
+D = rowsum(dO o O) -- and its dK/dV kernel) over the workload's synthetic
 inputs, which are resident in HBM before the timed region starts.  The
 default 30 untimed warm-up steps (about 60 ms of work) let the clocks settle:
 after only 5 the timed mean of 20 steps is about 4 % higher.  FLOPs are
@@ -388,7 +389,7 @@ def bench_dropout(fa, w, tensors, mask, steps, warmup, p, plain_ms):
            "fwd_tflops": round(f_fwd / (mean(fwd_ms) * 1e-3) / 1e12, 2),
            "bwd_tflops": round(tf_bwd, 2),
            "step_time_vs_plain": round(ms_step / plain_ms, 3),
-           "roofline": {"bound": "mfma", "kernel": "fa_backward_dropout (bwd_pre + bwd_dkdv + bwd_dq)",
+           "roofline": {"bound": "mfma", "kernel": "fa_backward_dropout (bwd_dq + bwd_dkdv)",
                         "achieved": round(tf_bwd, 2), "peak": peak, "unit": "TFLOP/s",
                         "frac": round(tf_bwd / peak, 4),
                         "traffic": None if rec is None else rec["bytes_per_call"].get("dropout_backward"),
@@ -445,7 +446,7 @@ def main():
     # Dominant work by time: the backward call (its kernels run back to back
     # on the stream, timed together) when present, else the forward kernel.
     if w.backward and mean(bwd_ms) >= mean(fwd_ms):
-        dom, dom_key, dom_ms, dom_flops = ("fa_backward (bwd_pre + bwd_dkdv + bwd_dq)", "backward",
+        dom, dom_key, dom_ms, dom_flops = ("fa_backward (bwd_dq + bwd_dkdv)", "backward",
                                            mean(bwd_ms), f_bwd)
     else:
         dom, dom_key, dom_ms, dom_flops = "fa_forward (fwd kernel)", "forward", mean(fwd_ms), f_fwd

@@ -8,10 +8,7 @@
 //   P = exp(scale*QK^T - lse),  dV = P^T dO,  dP = dO V^T,
 //   D_i = sum_c dO_ic O_ic,  dS = P o (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
 //
-// Three kernels, no atomics:
-//   bwd_pre:  per row, -D = -rowsum(dO o O) and the log2-domain statistic
-//     lse * log2(e) (+inf for rows with no visible key, so P = 0 there), both
-//     fp32, into the workspace.
+// Two kernels, no atomics, dQ first:
 //   bwd_dkdv_u: one workgroup per (key tile of 128, batch*head).  Wave w owns
 //     32 keys, keeps their K and V rows as MFMA operands and dK, dV in fp32
 //     accumulators, and streams the 64-row query tiles that can see them
@@ -24,7 +21,11 @@
 //   bwd_dq_u: one workgroup per (query tile of 128, batch*head), the
 //     forward's layout: S^T = K Q^T and dP^T = V dO^T with the query in the
 //     lane (so the statistic and D are per-lane scalars), dS^T in registers,
-//     and dQ^T += K^T dS^T with K read transposed; dQ is stored once.
+//     and dQ^T += K^T dS^T with K read transposed; dQ is stored once.  Its
+//     prologue computes each row's D = rowsum(dO o O) from the dO and O rows
+//     it loads anyway, and stores -D and the log2-domain statistic
+//     lse * log2(e) (+inf for rows with no visible key, so P = 0 there) into
+//     the workspace for bwd_dkdv_u, launched after it.
 // Recomputing S, P, dP in both kernels costs two extra products per score,
 // instead of the global atomic adds a single-pass dQ would need (those
 // execute at memory on this part and moved more bytes than the pass computes).
@@ -41,32 +42,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 template <int V>
 using ic = std::integral_constant<int, V>;
-
-template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO,
-                                                      const float* __restrict__ lse,
-                                                      float* __restrict__ neg_delta, float* __restrict__ lse2,
-                                                      size_t rows) {
-  using VT = typename V8<T>::t;
-  constexpr int LPR = D / 8;  // lanes per row, 8 elements each
-  const size_t gt = (size_t)blockIdx.x * 256 + threadIdx.x;
-  const size_t row = gt / LPR;
-  const int part = (int)(gt % LPR);
-  float acc = 0.f;
-  if (row < rows) {
-    const VT a = *(const VT*)(O + row * D + part * 8);
-    const VT b = *(const VT*)(dO + row * D + part * 8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
-  }
-#pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && part == 0) {
-    neg_delta[row] = -acc;
-    const float l = lse[row];
-    lse2[row] = l == -INFINITY ? INFINITY : l * kLog2e;
-  }
-}
 
 // ---- unit-pipelined kernels (d = 64: 2 waves per SIMD; d = 128: 1) ----
 //
@@ -441,6 +416,7 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dq_u_kernel(BwdParams
   const T* __restrict__ K = (const T*)p.k + base;
   const T* __restrict__ V = (const T*)p.v + base;
   const T* __restrict__ dO = (const T*)p.dO + base;
+  const T* __restrict__ O = (const T*)p.o + base;
   const int q0 = qt * BR + wave * 32;
   const int my_q = q0 + l32;
   const float c = p.scale_log2e;
@@ -511,15 +487,30 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dq_u_kernel(BwdParams
       issue(K, jq[t], t);
       issue(V, jq[t], NK + t);
     }
-  VT qf[DS], dof[DS];
+  VT qf[DS], dof[DS], of[DS];
 #pragma unroll
   for (int ds = 0; ds < DS; ++ds) {
     qf[ds] = my_q < N ? *(const VT*)(Q + (size_t)my_q * D + 16 * ds + 8 * g) : VT{};
     dof[ds] = my_q < N ? *(const VT*)(dO + (size_t)my_q * D + 16 * ds + 8 * g) : VT{};
+    of[ds] = my_q < N ? *(const VT*)(O + (size_t)my_q * D + 16 * ds + 8 * g) : VT{};
   }
-  // +inf statistic makes P = 0 on padding rows.
-  const float lq = my_q < N ? p.lse2[(size_t)bh * N + my_q] : INFINITY;
-  const float nd_row = my_q < N ? p.neg_delta[(size_t)bh * N + my_q] : 0.f;  // -D
+  // Row statistics of this lane's query: D = sum_c dO_c O_c (this lane holds
+  // half of the row, lane ^ 32 the other half) and lse * log2(e), +inf where
+  // lse = -inf (no visible key) and on padding rows, so that P = 0 there.
+  // Lanes 0..31 also store -D and the log2 statistic for the dK/dV kernel,
+  // which runs after this one.
+  float dpart = 0.f;
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dpart = fmaf((float)of[ds][e], (float)dof[ds][e], dpart);
+  const float nd_row = -half_swap_sum(dpart);  // -D
+  const float lse_q = my_q < N ? p.lse[(size_t)bh * N + my_q] : -INFINITY;
+  const float lq = lse_q == -INFINITY ? INFINITY : lse_q * kLog2e;
+  if (g == 0 && my_q < N) {
+    p.neg_delta[(size_t)bh * N + my_q] = nd_row;
+    p.lse2[(size_t)bh * N + my_q] = lq;
+  }
 
   f32x16 acc[DB];
 #pragma unroll
@@ -666,17 +657,13 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dq_u_kernel(BwdParams
 
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
-  const size_t rows = (size_t)p.BH * p.N;
-  const size_t threads = rows * (D / 8);
-  bwd_pre_kernel<T, D><<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st>>>(
-      (const T*)p.o, (const T*)p.dO, p.lse, p.neg_delta, p.lse2, rows);
+  // The dQ kernel also writes the row statistics (-D, lse * log2 e) that the
+  // dK/dV kernel reads, so it runs first.
+  const dim3 grid(((p.N + 127) / 128) * p.BH), block(256);
+  bwd_dq_u_kernel<T, D, CAUSAL, SPARSE, DROP><<<grid, block, 0, st>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 grid(((p.N + 127) / 128) * p.BH), block(256);
   bwd_dkdv_u_kernel<T, D, CAUSAL, SPARSE, DROP><<<grid, block, 0, st>>>(p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  bwd_dq_u_kernel<T, D, CAUSAL, SPARSE, DROP><<<grid, block, 0, st>>>(p);
   return hipGetLastError();
 }
 
