@@ -97,3 +97,46 @@ def test_backward_named_large_workloads(fa, name):
     assert (sdv - sdo).abs().max().item() <= 1e-2 * scale_dv
     for t in (dq, dk, dv):
         assert torch.isfinite(t).all()
+
+
+STATS = [
+    # B, H, N, d, dtype, causal, sparse, dropout_p
+    (2, 3, 130, 64, "bf16", True, False, 0.0),
+    (1, 2, 449, 128, "f16", False, False, 0.0),
+    (1, 2, 700, 64, "bf16", False, True, 0.0),
+    (1, 1, 300, 64, "bf16", True, False, 0.1),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype,causal,sparse,dropout_p", STATS)
+def test_backward_row_statistics(fa, B, H, N, d, dtype, causal, sparse, dropout_p):
+    """The per-row terms the backward computes before its gradient products:
+    D_i = sum_c dO_ic O_ic and the log2-domain statistic lse_i * log2(e).
+    They are left in the caller's workspace, two fp32 (B, H, N) arrays, each
+    padded to 256 bytes (-D first); D is compared with the oracle's row sum
+    over the same O and dO, the statistic with lse * log2(e) in fp32 (+inf
+    where lse = -inf)."""
+    import oracle
+    q, k, v, do = W.draw_qkvdo(B, H, N, d, dtype, seed=N * 5 + d + B)
+    mask = random_block_mask(N, 0.4, seed=N + 9) if sparse else None
+    scale = W.scale_for(d)
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    md = None if mask is None else mask.cuda()
+    kw = dict(dropout_p=dropout_p, seed=7, offset=0) if dropout_p else {}
+    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale, block_mask=md, **kw)
+    ws = torch.full((fa.workspace_size(B, H, N, d),), 0xFF, dtype=torch.uint8, device="cuda")
+    fa.backward(qd, kd, vd, o, lse, dod, causal=causal, scale=scale, block_mask=md,
+                workspace=ws, **kw)
+    torch.cuda.synchronize()
+    rows = B * H * N
+    second = (rows * 4 + 255) // 256 * 256
+    neg_d = ws[:rows * 4].view(torch.float32).cpu().reshape(B, H, N)
+    lse2 = ws[second:second + rows * 4].view(torch.float32).cpu().reshape(B, H, N)
+    ref_d = oracle.rowsum_do_o(f64(do), f64(o.cpu()))
+    assert_close("D", -f64(neg_d), ref_d, 1e-4 * max(1.0, float(np.abs(ref_d).max())))
+    lse_c = lse.cpu()
+    want = torch.where(torch.isneginf(lse_c), torch.full_like(lse_c, float("inf")),
+                       lse_c * torch.tensor(1.4426950408889634, dtype=torch.float32))
+    assert torch.equal(torch.isinf(lse2), torch.isinf(want))
+    fin = torch.isfinite(want)
+    assert (lse2[fin] - want[fin]).abs().max().item() <= 1e-6 * max(1.0, want[fin].abs().max().item())
