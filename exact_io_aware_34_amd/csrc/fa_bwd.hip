@@ -580,7 +580,7 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dq_u_kernel(BwdParams
     sdp(kslc, vslc, h, s_nxt, dp_nxt);
     dqacc(gslc, h, ds_p);
     dscores(ks, s_cur, dp_cur, ds_c);
-    if constexpr (D == 64 && !DROP) sched_interleave<12, 8, 1, 6>();
+    if constexpr (D == 64 && !DROP) sched_interleave<12, 0, 2, 6>();
     keep_here(ds_c);
   };
 
