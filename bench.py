@@ -161,17 +161,19 @@ def time_passes(fa, w, tensors, mask, steps, warmup, dropout_p=0.0, seed=0):
     import torch
     q, k, v, do, o, lse, ws, grads = tensors
     stream = torch.cuda.current_stream()
+    # With dropout the forward also writes O in fp32 for the backward's D.
+    o_acc = torch.empty(q.shape, dtype=torch.float32, device=q.device) if dropout_p else None
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
         fa.forward(q, k, v, causal=w.causal, scale=w.scale, block_mask=mask, out=o, lse=lse,
-                   dropout_p=dropout_p, seed=seed)
+                   dropout_p=dropout_p, seed=seed, o_acc=o_acc)
         if ev is not None:
             ev[1].record(stream)
         if w.backward:
             fa.backward(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, block_mask=mask,
-                        workspace=ws, grads=grads, dropout_p=dropout_p, seed=seed)
+                        workspace=ws, grads=grads, dropout_p=dropout_p, seed=seed, o_acc=o_acc)
         if ev is not None:
             ev[2].record(stream)
 

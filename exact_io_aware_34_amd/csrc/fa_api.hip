@@ -88,12 +88,13 @@ bool dropout_args(float p, uint64_t seed, uint32_t offset, uint32_t& k0, uint32_
 
 int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                  int N, int d, float scale, int causal, const uint8_t* block_mask, int dtype,
-                 float dropout_p, uint64_t seed, uint32_t offset, void* stream);
+                 bool drop, float dropout_p, uint64_t seed, uint32_t offset, float* o_acc,
+                 void* stream);
 int backward_impl(const void* q, const void* k, const void* v, const void* o, const void* dO,
                   const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, int d,
-                  float scale, int causal, const uint8_t* block_mask, int dtype, float dropout_p,
-                  uint64_t seed, uint32_t offset, void* workspace, size_t workspace_bytes,
-                  void* stream);
+                  float scale, int causal, const uint8_t* block_mask, int dtype, bool drop,
+                  float dropout_p, uint64_t seed, uint32_t offset, const float* o_acc,
+                  void* workspace, size_t workspace_bytes, void* stream);
 
 // FP8 workspace regions, in order, each padded to 256 bytes.
 struct Fp8Layout {
@@ -149,7 +150,7 @@ int fp8_setup(fa::Fp8Params& p, const void* q, const void* k, const void* v, int
 
 extern "C" {
 
-int fa_abi_version(void) { return 2; }
+int fa_abi_version(void) { return 3; }
 
 const char* fa_status_string(int status) {
   switch (status) {
@@ -165,16 +166,16 @@ const char* fa_status_string(int status) {
 int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int N, int d, float scale, int causal,
                const uint8_t* block_mask, int dtype, void* stream) {
-  return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, dtype, 0.f, 0, 0,
-                      stream);
+  return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, dtype, false, 0.f, 0,
+                      0, nullptr, stream);
 }
 
 int fa_forward_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
                        int B, int H, int N, int d, float scale, int causal,
                        const uint8_t* block_mask, int dtype, float dropout_p, uint64_t seed,
-                       uint32_t offset, void* stream) {
-  return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, dtype, dropout_p,
-                      seed, offset, stream);
+                       uint32_t offset, float* o_acc, void* stream) {
+  return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, dtype, true,
+                      dropout_p, seed, offset, o_acc, stream);
 }
 
 }  // extern "C"
@@ -183,10 +184,12 @@ namespace {
 
 int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                  int N, int d, float scale, int causal, const uint8_t* block_mask, int dtype,
-                 float dropout_p, uint64_t seed, uint32_t offset, void* stream) {
+                 bool drop, float dropout_p, uint64_t seed, uint32_t offset, float* o_acc,
+                 void* stream) {
   if (!tensor_ptr_ok(q) || !tensor_ptr_ok(k) || !tensor_ptr_ok(v) || !tensor_ptr_ok(o))
     return FA_ERR_INVALID_ARG;
   if (lse == nullptr || !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
+  if (o_acc != nullptr && !aligned(o_acc, 16)) return FA_ERR_INVALID_ARG;
   const int rc = check_common(B, H, N, d, scale, dtype);
   if (rc != FA_OK) return rc;
   if (block_mask != nullptr && (N + fa::MASK_TILE - 1) / fa::MASK_TILE > fa::FWD_MAX_MASK_TILES)
@@ -207,7 +210,11 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   if (!dropout_args(dropout_p, seed, offset, p.drop_k0, p.drop_k1, p.drop_off, p.drop_t8,
                     p.drop_scale))
     return FA_ERR_INVALID_ARG;
-  if (p.drop_t8 > 0 && dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  // The dropout kernels run when something is dropped or the fp32 O is asked
+  // for; with nothing dropped and no fp32 O the plain kernel gives the same O.
+  p.drop = drop && (p.drop_t8 > 0 || o_acc != nullptr);
+  p.o_acc = o_acc;
+  if (p.drop && dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   const hipError_t e = fa::launch_forward(p, dtype, d, causal != 0, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -261,8 +268,8 @@ int fa_forward_split(const void* q, const void* k, const void* v, void* o, float
   if (rc != FA_OK) return rc;
   const int n = forward_split_count(B, H, N, d, n_splits);
   if (n <= 1)
-    return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, dtype, 0.f, 0, 0,
-                        stream);
+    return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, dtype, false, 0.f,
+                        0, 0, nullptr, stream);
   if (!tensor_ptr_ok(q) || !tensor_ptr_ok(k) || !tensor_ptr_ok(v) || !tensor_ptr_ok(o))
     return FA_ERR_INVALID_ARG;
   if (lse == nullptr || !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
@@ -317,16 +324,17 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
                 const uint8_t* block_mask, int dtype,
                 void* workspace, size_t workspace_bytes, void* stream) {
   return backward_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, block_mask,
-                       dtype, 0.f, 0, 0, workspace, workspace_bytes, stream);
+                       dtype, false, 0.f, 0, 0, nullptr, workspace, workspace_bytes, stream);
 }
 
-int fa_backward_dropout(const void* q, const void* k, const void* v, const void* o,
+int fa_backward_dropout(const void* q, const void* k, const void* v, const float* o_acc,
                         const void* dO, const float* lse, float* dq, float* dk, float* dv,
                         int B, int H, int N, int d, float scale, int causal,
                         const uint8_t* block_mask, int dtype, float dropout_p, uint64_t seed,
                         uint32_t offset, void* workspace, size_t workspace_bytes, void* stream) {
-  return backward_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, block_mask,
-                       dtype, dropout_p, seed, offset, workspace, workspace_bytes, stream);
+  return backward_impl(q, k, v, o_acc, dO, lse, dq, dk, dv, B, H, N, d, scale, causal,
+                       block_mask, dtype, true, dropout_p, seed, offset, o_acc, workspace,
+                       workspace_bytes, stream);
 }
 
 int fa_dropout_mask(int B, int H, int N, float dropout_p, uint64_t seed, uint32_t offset,
@@ -351,9 +359,9 @@ namespace {
 
 int backward_impl(const void* q, const void* k, const void* v, const void* o, const void* dO,
                   const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, int d,
-                  float scale, int causal, const uint8_t* block_mask, int dtype, float dropout_p,
-                  uint64_t seed, uint32_t offset, void* workspace, size_t workspace_bytes,
-                  void* stream) {
+                  float scale, int causal, const uint8_t* block_mask, int dtype, bool drop,
+                  float dropout_p, uint64_t seed, uint32_t offset, const float* o_acc,
+                  void* workspace, size_t workspace_bytes, void* stream) {
   if (!tensor_ptr_ok(q) || !tensor_ptr_ok(k) || !tensor_ptr_ok(v) || !tensor_ptr_ok(o) ||
       !tensor_ptr_ok(dO) || !tensor_ptr_ok(dq) || !tensor_ptr_ok(dk) || !tensor_ptr_ok(dv))
     return FA_ERR_INVALID_ARG;
@@ -361,6 +369,8 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
   const int rc = check_common(B, H, N, d, scale, dtype);
   if (rc != FA_OK) return rc;
   if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (block_mask != nullptr && (N + fa::MASK_TILE - 1) / fa::MASK_TILE > fa::FWD_MAX_MASK_TILES)
+    return FA_ERR_UNSUPPORTED;
   if (workspace == nullptr || !aligned(workspace, 16) ||
       workspace_bytes < fa_backward_workspace_size(B, H, N, d))
     return FA_ERR_WORKSPACE;
@@ -385,6 +395,8 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
   if (!dropout_args(dropout_p, seed, offset, p.drop_k0, p.drop_k1, p.drop_off, p.drop_t8,
                     p.drop_scale))
     return FA_ERR_INVALID_ARG;
+  p.drop = drop;
+  p.o_acc = o_acc;
   const hipError_t e = fa::launch_backward(p, dtype, d, causal != 0, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

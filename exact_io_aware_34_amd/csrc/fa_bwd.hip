@@ -416,7 +416,6 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dq_u_kernel(BwdParams
   const T* __restrict__ K = (const T*)p.k + base;
   const T* __restrict__ V = (const T*)p.v + base;
   const T* __restrict__ dO = (const T*)p.dO + base;
-  const T* __restrict__ O = (const T*)p.o + base;
   const int q0 = qt * BR + wave * 32;
   const int my_q = q0 + l32;
   const float c = p.scale_log2e;
@@ -487,23 +486,43 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dq_u_kernel(BwdParams
       issue(K, jq[t], t);
       issue(V, jq[t], NK + t);
     }
-  VT qf[DS], dof[DS], of[DS];
+  VT qf[DS], dof[DS];
 #pragma unroll
   for (int ds = 0; ds < DS; ++ds) {
     qf[ds] = my_q < N ? *(const VT*)(Q + (size_t)my_q * D + 16 * ds + 8 * g) : VT{};
     dof[ds] = my_q < N ? *(const VT*)(dO + (size_t)my_q * D + 16 * ds + 8 * g) : VT{};
-    of[ds] = my_q < N ? *(const VT*)(O + (size_t)my_q * D + 16 * ds + 8 * g) : VT{};
   }
   // Row statistics of this lane's query: D = sum_c dO_c O_c (this lane holds
   // half of the row, lane ^ 32 the other half) and lse * log2(e), +inf where
   // lse = -inf (no visible key) and on padding rows, so that P = 0 there.
   // Lanes 0..31 also store -D and the log2 statistic for the dK/dV kernel,
-  // which runs after this one.
+  // which runs after this one.  With dropout O is read in fp32: its kept
+  // terms carry 1/(1 - p), and on a row with one visible key
+  // dS = P (dP/(1 - p) - D) cancels exactly only if D does not carry O's
+  // rounding to 16 bits.
   float dpart = 0.f;
+  if constexpr (DROP) {
+    const float* __restrict__ OA = p.o_acc + base;
 #pragma unroll
-  for (int ds = 0; ds < DS; ++ds)
+    for (int ds = 0; ds < DS; ++ds) {
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+      if (my_q < N) {
+        a = *(const float4*)(OA + (size_t)my_q * D + 16 * ds + 8 * g);
+        b = *(const float4*)(OA + (size_t)my_q * D + 16 * ds + 8 * g + 4);
+      }
+      const float ov[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dpart = fmaf((float)of[ds][e], (float)dof[ds][e], dpart);
+      for (int e = 0; e < 8; ++e) dpart = fmaf(ov[e], (float)dof[ds][e], dpart);
+    }
+  } else {
+    const T* __restrict__ O = (const T*)p.o + base;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      const VT of = my_q < N ? *(const VT*)(O + (size_t)my_q * D + 16 * ds + 8 * g) : VT{};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dpart = fmaf((float)of[e], (float)dof[ds][e], dpart);
+    }
+  }
   const float nd_row = -half_swap_sum(dpart);  // -D
   const float lse_q = my_q < N ? p.lse[(size_t)bh * N + my_q] : -INFINITY;
   const float lq = lse_q == -INFINITY ? INFINITY : lse_q * kLog2e;
@@ -669,7 +688,7 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
 
 template <typename T, int D>
 hipError_t launch_bwd(const BwdParams& p, bool causal, bool sparse, hipStream_t st) {
-  if (p.drop_t8 > 0) {
+  if (p.drop) {
     if (causal && sparse) return launch_bwd_t<T, D, true, true, true>(p, st);
     if (causal) return launch_bwd_t<T, D, true, false, true>(p, st);
     if (sparse) return launch_bwd_t<T, D, false, true, true>(p, st);

@@ -402,6 +402,19 @@ __global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p)
         for (int e = 0; e < 4; ++e) hv[e] = (T)(o[db][4 * rg + e] * inv);
         *(HT*)(orow + 32 * db + 8 * rg + 4 * g) = hv;
       }
+    if constexpr (DROP) {
+      // The unrounded O, for the dropout backward's D = rowsum(dO o O).
+      if (p.o_acc != nullptr) {
+        float* arow = p.o_acc + base + (size_t)q * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg)
+            *(float4*)(arow + 32 * db + 8 * rg + 4 * g) =
+                make_float4(o[db][4 * rg] * inv, o[db][4 * rg + 1] * inv,
+                            o[db][4 * rg + 2] * inv, o[db][4 * rg + 3] * inv);
+      }
+    }
     if (g == 0) p.lse[(size_t)bh * N + q] = lt > 0.f ? m_run * p.scale + logf(lt) : -INFINITY;
   }
 }
@@ -563,8 +576,7 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(FwdParams p) {
 template <typename T, int D>
 hipError_t launch16(const FwdParams& p, bool causal, bool sparse, hipStream_t st) {
   dim3 grid(((p.N + 127) / 128) * p.BH * (p.n_splits > 1 ? p.n_splits : 1)), block(256);
-  const bool drop = p.drop_t8 > 0;
-  if (drop) {
+  if (p.drop) {
     if (causal && sparse) fwd16_kernel<T, D, true, true, true><<<grid, block, 0, st>>>(p);
     else if (causal) fwd16_kernel<T, D, true, false, true><<<grid, block, 0, st>>>(p);
     else if (sparse) fwd16_kernel<T, D, false, true, true><<<grid, block, 0, st>>>(p);

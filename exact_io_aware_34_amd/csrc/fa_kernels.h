@@ -47,6 +47,11 @@ struct FwdParams {
   // 1 / (1 - drop_t8 / 256).
   uint32_t drop_k0, drop_k1, drop_off, drop_t8;
   float drop_scale;
+  // drop != 0 runs the dropout kernels (also with drop_t8 = 0, which keeps
+  // every element); they also store O in fp32 to o_acc (B*H, N, d) before its
+  // rounding to the input type, when o_acc is not null.
+  int drop;
+  float* o_acc;
   // Split key ranges (16-bit inputs, no dropout): n_splits > 1 cuts every
   // query tile's key range into n_splits equal runs of tiles, each its own
   // workgroup, which writes its normalised partial output and logsumexp to
@@ -75,6 +80,10 @@ struct BwdParams {
   float scale, scale_log2e;
   uint32_t drop_k0, drop_k1, drop_off, drop_t8;  // dropout as in FwdParams
   float drop_scale;
+  // drop != 0 runs the dropout kernels; D_i then comes from o_acc, the
+  // forward's fp32 O (B*H, N, d), and o is not read.
+  int drop;
+  const float* o_acc;
 };
 
 struct DecParams {

@@ -48,7 +48,7 @@ _lib.fa_forward_fp8_workspace_size.argtypes = [_i, _i, _i, _i]
 _lib.fa_forward_fp8_workspace_size.restype = ctypes.c_size_t
 _u64, _u32 = ctypes.c_uint64, ctypes.c_uint32
 _lib.fa_forward_dropout.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _i, _f,
-                                    _u64, _u32, _vp]
+                                    _u64, _u32, _vp, _vp]
 _lib.fa_forward_dropout.restype = _i
 _lib.fa_backward_dropout.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
                                      _f, _i, _vp, _i, _f, _u64, _u32, _vp, ctypes.c_size_t, _vp]
@@ -109,6 +109,24 @@ def _check_inputs(*ts):
         raise ValueError(f"unsupported dtype {ref.dtype}")
 
 
+def _check_f32(t, shape, name):
+    """A caller-supplied fp32 GPU tensor the kernels write or read in full."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous float32 of shape {tuple(shape)}")
+
+
+def _check_workspace(workspace):
+    if workspace is None:
+        return 0
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda:
+        raise ValueError("workspace must be a GPU tensor")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return workspace.numel() * workspace.element_size()
+
+
 def _mask_arg(block_mask, n):
     if block_mask is None:
         return None
@@ -134,11 +152,14 @@ def forward_split_workspace_size(B, H, N, d, n_splits=0) -> int:
 
 
 def forward(q, k, v, causal=False, scale=None, block_mask=None, out=None, lse=None,
-            stream=None, dropout_p=0.0, seed=0, offset=0, n_splits=1, workspace=None):
+            stream=None, dropout_p=0.0, seed=0, offset=0, n_splits=1, workspace=None,
+            o_acc=None):
     """Exact attention forward: returns (o, lse) with o in q's dtype, lse fp32.
-    dropout_p > 0 drops probabilities with the mask fa_dropout_mask describes.
-    n_splits != 1 runs fa_forward_split (0 = the library's choice of key runs)
-    with `workspace` (allocated here when None)."""
+    dropout_p > 0 drops probabilities with the mask fa_dropout_mask describes;
+    `o_acc` (fp32, q's shape) then receives O before its rounding to q's
+    dtype, which the dropout backward needs.  n_splits != 1 runs
+    fa_forward_split (0 = the library's choice of key runs) with `workspace`
+    (allocated here when None)."""
     _check_inputs(q, k, v)
     B, H, N, d = q.shape
     scale = default_scale(d) if scale is None else float(scale)
@@ -146,22 +167,24 @@ def forward(q, k, v, causal=False, scale=None, block_mask=None, out=None, lse=No
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     _check_inputs(q, o)
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 (B, H, N)")
+    _check_f32(lse, (B, H, N), "lse")
+    if o_acc is not None:
+        _check_f32(o_acc, (B, H, N, d), "o_acc")
     if n_splits != 1:
-        if dropout_p:
+        if dropout_p or o_acc is not None:
             raise ValueError("split key runs are not offered with dropout")
         ws_bytes = forward_split_workspace_size(B, H, N, d, n_splits)
         if workspace is None and ws_bytes > 0:
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-        nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        nbytes = _check_workspace(workspace)
         rc = _lib.fa_forward_split(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                                    scale, int(bool(causal)), _ptr(mask), DTYPE_CODES[q.dtype],
                                    int(n_splits), _ptr(workspace), nbytes, _stream(stream))
-    elif dropout_p:
+    elif dropout_p or o_acc is not None:
         rc = _lib.fa_forward_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                                      scale, int(bool(causal)), _ptr(mask), DTYPE_CODES[q.dtype],
-                                     float(dropout_p), int(seed), int(offset), _stream(stream))
+                                     float(dropout_p), int(seed), int(offset), _ptr(o_acc),
+                                     _stream(stream))
     else:
         rc = _lib.fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                              scale, int(bool(causal)), _ptr(mask), DTYPE_CODES[q.dtype],
@@ -176,26 +199,36 @@ def workspace_size(B, H, N, d) -> int:
 
 
 def backward(q, k, v, o, lse, do, causal=False, scale=None, block_mask=None,
-             workspace=None, grads=None, stream=None, dropout_p=0.0, seed=0, offset=0):
+             workspace=None, grads=None, stream=None, dropout_p=0.0, seed=0, offset=0,
+             o_acc=None):
     """Exact attention backward: returns fp32 (dq, dk, dv).  With dropout,
-    pass the forward's (dropout_p, seed, offset) so the same mask applies."""
+    pass the forward's (dropout_p, seed, offset) so the same mask applies, and
+    its fp32 output `o_acc` (required then; `o` is not read)."""
     _check_inputs(q, k, v, o, do)
     B, H, N, d = q.shape
     scale = default_scale(d) if scale is None else float(scale)
     mask = _mask_arg(block_mask, N)
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 (B, H, N)")
+    _check_f32(lse, (B, H, N), "lse")
+    drop = bool(dropout_p) or o_acc is not None
+    if drop:
+        if o_acc is None:
+            raise ValueError("the dropout backward needs the forward's fp32 output o_acc")
+        _check_f32(o_acc, (B, H, N, d), "o_acc")
     if grads is None:
         grads = tuple(torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
                       for _ in range(3))
+    if len(grads) != 3:
+        raise ValueError("grads must be a (dq, dk, dv) tuple")
+    for name, g in zip(("dq", "dk", "dv"), grads):
+        _check_f32(g, (B, H, N, d), name)
     ws_bytes = workspace_size(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     dq, dk, dv = grads
-    ws_n = workspace.numel() * workspace.element_size()
-    if dropout_p:
-        rc = _lib.fa_backward_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
-                                      _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, scale,
+    ws_n = _check_workspace(workspace)
+    if drop:
+        rc = _lib.fa_backward_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o_acc), _ptr(do),
+                                      _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, scale,
                                       int(bool(causal)), _ptr(mask), DTYPE_CODES[q.dtype],
                                       float(dropout_p), int(seed), int(offset), _ptr(workspace),
                                       ws_n, _stream(stream))
@@ -236,12 +269,11 @@ def decode(q, k, v, causal=False, scale=None, n_splits=0, out=None, lse=None, wo
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
     if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous():
         raise ValueError("out must be contiguous, shaped and typed like q")
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 (B, H, Nq)")
+    _check_f32(lse, (B, H, Nq), "lse")
     ws_bytes = decode_workspace_size(B, H, Nq, Nk, d, n_splits)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    nbytes = _check_workspace(workspace)
     rc = _lib.fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, scale,
                         int(bool(causal)), int(n_splits), DTYPE_CODES[q.dtype], _ptr(workspace),
                         nbytes, _stream(stream))
@@ -263,6 +295,7 @@ def _fp8_args(q, k, v, signs, workspace):
     ws_bytes = fp8_workspace_size(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace)
     return workspace
 
 
@@ -303,8 +336,7 @@ def forward_fp8(q, k, v, signs=None, causal=False, scale=None, block_mask=None, 
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     _check_inputs(q, o)
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 (B, H, N)")
+    _check_f32(lse, (B, H, N), "lse")
     rc = _lib.fa_forward_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, scale,
                              int(bool(causal)), _ptr(mask), DTYPE_CODES[q.dtype], _ptr(signs),
                              _ptr(workspace), workspace.numel() * workspace.element_size(),

@@ -123,7 +123,8 @@ size_t fa_backward_workspace_size(int B, int H, int N, int d);
  *   dS = P o (dP - D),  dP = dO V^T,  D_i = sum_c dO_ic * o_ic.
  * `workspace` is a device buffer of at least fa_backward_workspace_size() bytes,
  * owned by the caller, scratch for the duration of the call.
- * Supported: d in {64, 128}; dtype FA_F16, FA_BF16 (FA_F32 -> FA_ERR_UNSUPPORTED).
+ * Supported: d in {64, 128}; dtype FA_F16, FA_BF16 (FA_F32 -> FA_ERR_UNSUPPORTED);
+ * with a block_mask, N <= 262144 (2048 mask tiles), else FA_ERR_UNSUPPORTED.
  */
 int fa_backward(const void* q, const void* k, const void* v, const void* o,
                 const void* dO, const float* lse,
@@ -152,15 +153,26 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
  * with the same (dropout_p, seed, offset).
  *
  * Arguments as fa_forward / fa_backward plus dropout_p (finite, 0 <= p < 1,
- * else FA_ERR_INVALID_ARG), seed and offset.  p = 0 (t = 0) is the plain
- * path.  FA_F32 with p > 0 -> FA_ERR_UNSUPPORTED.
+ * else FA_ERR_INVALID_ARG), seed and offset, and the output O in fp32:
+ *   - fa_forward_dropout writes it to `o_acc` ((B,H,N,d) fp32, device,
+ *     caller-owned, 16-byte aligned) when o_acc is not NULL: O before its
+ *     rounding to dtype.  NULL skips it (a caller that runs no backward).
+ *   - fa_backward_dropout takes that fp32 O in place of the 16-bit o
+ *     (required, non-NULL, 16-byte aligned) and computes D from it.  The
+ *     reason: a causal row with one visible key has dS = P (dP/(1-p) - D) = 0
+ *     exactly, but D from O rounded to 16 bits leaves that rounding, times
+ *     the uncancelled 1/(1-p), in dQ (measured up to 1.9e-2 at d = 128,
+ *     p = 0.2 against the exact gradient).
+ * With p = 0 (t = 0) nothing is dropped and the result is the plain one.
+ * FA_F32 -> FA_ERR_UNSUPPORTED (also at p = 0 with o_acc, or in the
+ * backward).  With a block_mask, N <= 262144 as for fa_forward / fa_backward.
  */
 int fa_forward_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
                        int B, int H, int N, int d, float scale, int causal,
                        const uint8_t* block_mask, int dtype, float dropout_p, uint64_t seed,
-                       uint32_t offset, void* stream);
+                       uint32_t offset, float* o_acc, void* stream);
 
-int fa_backward_dropout(const void* q, const void* k, const void* v, const void* o,
+int fa_backward_dropout(const void* q, const void* k, const void* v, const float* o_acc,
                         const void* dO, const float* lse, float* dq, float* dk, float* dv,
                         int B, int H, int N, int d, float scale, int causal,
                         const uint8_t* block_mask, int dtype, float dropout_p, uint64_t seed,
@@ -274,7 +286,8 @@ size_t fa_forward_fp8_workspace_size(int B, int H, int N, int d);
 /* Static, human-readable text for a status code. */
 const char* fa_status_string(int status);
 
-/* Library ABI version (this header: 2; 2 added fa_forward_split*). */
+/* Library ABI version (this header: 3; 2 added fa_forward_split*, 3 the fp32
+ * output o_acc of the dropout calls). */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

@@ -66,9 +66,7 @@ from .fp8 import (  # noqa: F401
     e4m3,
     fp8_forward,
     fp8_forward_head,
-    fwht_f32,
     hadamard,
-    prepare_f32,
     rotate,
 )
 from .online import (  # noqa: F401

@@ -109,12 +109,12 @@ def forward_head_dropout(q, k, v, scale, p, seed, offset, bh, causal=False, bloc
 
 
 def backward_head_dropout(q, k, v, do, scale, p, seed, offset, bh, causal=False,
-                          block_mask=None, o=None):
+                          block_mask=None):
     """(dq, dk, dv) of one head with dropout, the mask held fixed.
 
-    `o` is the forward output the backward is given (D_i = sum_c dO_ic o_ic);
-    by default it is recomputed exactly.  A caller that stores O in a 16-bit
-    type passes that stored O, as the backward pass receives it.
+    Everything comes from q, k, v and dO: P from the scores, the output
+    O = (P o Z) V / (1 - p) that D_i = sum_c dO_ic O_ic needs is recomputed
+    here, exactly.
     """
     q, k, v, do = (np.asarray(t, dtype=np.float64) for t in (q, k, v, do))
     n = q.shape[0]
@@ -123,9 +123,8 @@ def backward_head_dropout(q, k, v, do, scale, p, seed, offset, bh, causal=False,
     pm, _ = _row_softmax(s, allowed(rows, n, causal, block_mask))
     zc = keep_mask(bh, rows, rows, seed, offset, p) * keep_scale(p)
     pd = pm * zc
-    if o is None:
-        o = pd @ v
-    d = np.sum(do * np.asarray(o, dtype=np.float64), axis=1)
+    o = pd @ v
+    d = np.sum(do * o, axis=1)
     dp = (do @ v.T) * zc
     ds = pm * (dp - d[:, None])
     return scale * ds @ k, scale * ds.T @ q, pd.T @ do

@@ -93,57 +93,19 @@ def block_quantize(x, block, quantize=e4m3):
     return x8, scales
 
 
-def fwht_f32(x):
-    """Fast Walsh-Hadamard transform of the rows of x in float32: butterfly
-    stages (a, b) -> (a + b, a - b) over index bit 0, 1, 2, ... in turn, each
-    result rounded to float32.  In exact arithmetic this is x H_d."""
-    y = np.array(x, dtype=np.float32)
-    d = y.shape[-1]
-    h = 1
-    while h < d:
-        y = y.reshape(y.shape[:-1] + (d // (2 * h), 2, h))
-        a, b = y[..., 0, :].copy(), y[..., 1, :].copy()
-        y[..., 0, :] = a + b
-        y[..., 1, :] = a - b
-        y = y.reshape(y.shape[:-3] + (d,))
-        h *= 2
-    return y
-
-
-def prepare_f32(x, signs, block=64):
-    """The quantisation decisions in float32 arithmetic: rows of the 16-bit
-    input x (converted exactly to float32) times the signs, transformed by
-    fwht_f32, times float32(1 / sqrt(d)); per block of rows amax,
-    inv = float32(448) / amax, codes e4m3(clamp(float32(x * inv), +-448)),
-    scale = float32(amax / 448) (1 for an all-zero block).  signs=None skips
-    the rotation.  Returns (codes as float64 values, scales as float64)."""
-    x = np.array(x, dtype=np.float32)
-    n, d = x.shape
-    if signs is not None:
-        x = fwht_f32(x * np.asarray(signs, np.float32)) * (np.float32(1) / np.sqrt(np.float32(d)))
-    nb = -(-n // block)
-    codes = np.zeros(x.shape)
-    scales = np.ones(nb)
-    for b in range(nb):
-        rows = slice(b * block, min(n, (b + 1) * block))
-        amax = np.float32(np.max(np.abs(x[rows])))
-        if amax > 0:
-            inv = np.float32(E4M3_MAX) / amax
-            y = np.clip((x[rows] * inv).astype(np.float32), -E4M3_MAX, E4M3_MAX)
-            codes[rows] = e4m3(y.astype(np.float64))
-            scales[b] = float(np.float32(amax / np.float32(E4M3_MAX)))
-    return codes, scales
-
-
 def fp8_forward_head(q, k, v, scale, causal=False, block_mask=None, signs=None, block=64,
-                     quantize=e4m3, rows=None):
+                     quantize=e4m3, rows=None, terms=False):
     """(o, lse) of one head by the FP8 method above (float64 emulation).
 
     signs=None skips the rotation (naive block-quantised FP8).  `quantize`
     is the rounding applied to every quantised operand; passing the identity
     turns the method into exact attention (a pin of the composition).
     `rows` restricts the output to those query rows (the operands are still
-    quantised whole).
+    quantised whole).  terms=True also returns the step-4 quantities as a
+    dict: p (the unrounded P_ij = exp(s_ij - m_i), 0 off the visible keys),
+    r (per key), v8, sv_max and l, with o = sv_max (e4m3(p r) @ v8) / l, and
+    s_abs = scale s_q s_k <|q8_i|, |k8_j|> (the scores' sum of absolute
+    products).
     """
     q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
     n, d = q.shape
@@ -172,6 +134,9 @@ def fp8_forward_head(q, k, v, scale, causal=False, block_mask=None, signs=None, 
         lse = m_safe + np.log(ell)
     o[empty] = 0.0
     lse[empty] = -np.inf
+    if terms:
+        s_abs = scale * (np.abs(q8[rows]) * rq[:, None]) @ (np.abs(k8) * rk[:, None]).T
+        return o, lse, {"p": p, "r": r, "v8": v8, "sv_max": sv_max, "l": ell, "s_abs": s_abs}
     return o, lse
 
 

@@ -15,9 +15,11 @@ scores so that the recurrence is tested in isolation from the products.
   same section (block max, block exponentials and sum, new global
   normalisers, output rescaled and renormalised by l_new at every block),
   which is also the order of the marketmaker.cc page's loop.
-* ``online_softmax_deferred``: the variant where O stays unnormalised, is
-  rescaled only by exp(m_old - m_new) and divided by l once at the end
-  (ultralytics.com's PyTorch loop; the "FA2" section of marketmaker.cc).
+* ``online_softmax_deferred``: the variant where O stays unnormalised: each
+  key block's own (max, sum, unnormalised output) is merged into the running
+  triple with the merge weights, and O is divided by l once at the end (the
+  deferred normalisation of the "FA2" section of marketmaker.cc; the
+  ultralytics.com glossary's loop computes the same quantity).
 
 When the running max is still -inf (no allowed key seen yet), the rescale
 factor exp(m_old - m_new) is taken as 1 instead of exp(-inf + inf) = NaN; a
@@ -79,22 +81,32 @@ def online_softmax_normalised_each_step(s, v, block, dtype=np.float64):
 def online_softmax_deferred(s, v, block, dtype=np.float64):
     """Same result, keeping O unnormalised until the last block.
 
+    Each key block b contributes its own statistics (m_b, l_b) and its own
+    unnormalised output u_b = sum_j exp(s_j - m_b) v_j; the running triple
+    (m, l, u) absorbs them with the two weights of the incremental-softmax
+    merge, exp(m - m_new) for what was there and exp(m_b - m_new) for the new
+    block ("Rastreamento Incremental do Softmax", xyznot.com, section
+    "Método").  Division by l happens once, after the last block (the
+    deferred normalisation of the "FA2" section of marketmaker.cc).
+
     Returns (o, m, l).  Rows with no allowed key return o = 0, l = 0.
     """
     s = np.asarray(s, dtype=dtype)
     v = np.asarray(v, dtype=dtype)
     r, n = s.shape
-    row_max = np.full((r, 1), -np.inf, dtype=dtype)
-    row_sum = np.zeros((r, 1), dtype=dtype)
-    out = np.zeros((r, v.shape[1]), dtype=dtype)
+    m = np.full(r, -np.inf, dtype=dtype)
+    ell = np.zeros(r, dtype=dtype)
+    u = np.zeros((r, v.shape[1]), dtype=dtype)
     for j0, j1 in _blocks(n, block):
-        scores = s[:, j0:j1]
-        new_max = np.maximum(row_max, scores.max(axis=1, keepdims=True))
-        rescale = _exp_diff(row_max, new_max).astype(dtype)
-        probs = _exp_diff(scores, new_max).astype(dtype)
-        probs = np.where(np.isneginf(scores), 0.0, probs).astype(dtype)
-        row_sum = row_sum * rescale + probs.sum(axis=1, keepdims=True)
-        out = out * rescale + probs @ v[j0:j1]
-        row_max = new_max
-    safe = np.where(row_sum > 0, row_sum, 1.0)
-    return (out / safe).astype(dtype), row_max[:, 0], row_sum[:, 0]
+        blk = s[:, j0:j1]
+        m_b = blk.max(axis=1)
+        e_b = np.where(np.isneginf(blk), 0.0, _exp_diff(blk, m_b[:, None])).astype(dtype)
+        l_b = e_b.sum(axis=1)
+        u_b = e_b @ v[j0:j1]
+        m_new, ell = merge_stats(m, ell, m_b, l_b)
+        w_old = _exp_diff(m, m_new).astype(dtype)[:, None]
+        w_new = _exp_diff(m_b, m_new).astype(dtype)[:, None]
+        u = (w_old * u + w_new * u_b).astype(dtype)
+        m, ell = m_new.astype(dtype), ell.astype(dtype)
+    o = u / np.where(ell > 0, ell, 1.0).astype(dtype)[:, None]
+    return o.astype(dtype), m, ell

@@ -37,7 +37,8 @@ def lib():
     L.fa_forward_fp8_workspace_size.argtypes = [i, i, i, i]
     L.fa_forward_fp8_workspace_size.restype = ctypes.c_size_t
     u64, u32 = ctypes.c_uint64, ctypes.c_uint32
-    L.fa_forward_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, f, u64, u32, vp]
+    L.fa_forward_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, f, u64, u32, vp,
+                                     vp]
     L.fa_backward_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i,
                                       f, u64, u32, vp, ctypes.c_size_t, vp]
     L.fa_dropout_mask.argtypes = [i, i, i, f, u64, u32, vp, vp]
@@ -67,7 +68,7 @@ def test_header_declares_the_boundary():
 def test_every_declared_symbol_is_exported(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.fa_abi_version() == 2
+    assert lib.fa_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -108,9 +109,9 @@ def test_forward_validation(lib):
     assert fwd(lib, N=1 << 30, d=64) == -2
 
 
-def bwd(lib, dtype=2, ws=FAKE, ws_bytes=1 << 30, d=64, dq=FAKE):
-    return lib.fa_backward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dq, FAKE, FAKE, 2, 3, 100, d,
-                           0.125, 1, None, dtype, ws, ws_bytes, None)
+def bwd(lib, dtype=2, ws=FAKE, ws_bytes=1 << 30, d=64, dq=FAKE, N=100, mask=None):
+    return lib.fa_backward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dq, FAKE, FAKE, 2, 3, N, d,
+                           0.125, 1, mask, dtype, ws, ws_bytes, None)
 
 
 def test_backward_validation(lib):
@@ -120,6 +121,20 @@ def test_backward_validation(lib):
     assert bwd(lib, dtype=0) == -2                      # fp32 backward not built
     assert bwd(lib, ws=None) == -3
     assert bwd(lib, ws_bytes=2 * 2 * 3 * 100 * 4 - 1) == -3
+
+
+def test_block_mask_size_limit(lib):
+    """A block mask covers at most 2048 x 2048 tiles (N <= 262144): every call
+    that takes one rejects a longer sequence before any launch."""
+    n_big = 2048 * 128 + 1
+    assert bwd(lib, N=n_big, mask=FAKE) == -2
+    assert lib.fa_backward_dropout(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 3,
+                                   n_big, 64, 0.125, 1, FAKE, 2, 0.1, 1, 0, FAKE, 1 << 40,
+                                   None) == -2
+    assert lib.fa_forward(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, n_big, 64, 0.125, 0, FAKE, 2,
+                          None) == -2
+    assert lib.fa_forward_dropout(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, n_big, 64, 0.125, 0, FAKE,
+                                  2, 0.1, 1, 0, None, None) == -2
 
 
 def test_decode_split_choice(lib):
@@ -215,16 +230,24 @@ def test_fp8_validation(lib):
 
 
 def test_dropout_validation(lib):
-    def fwd_d(p, dtype=2):
+    def fwd_d(p, dtype=2, o_acc=None):
         return lib.fa_forward_dropout(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 100, 64, 0.125, 0, None,
-                                      dtype, p, 1, 0, None)
+                                      dtype, p, 1, 0, o_acc, None)
     assert fwd_d(-0.1) == -1
     assert fwd_d(1.0) == -1
     assert fwd_d(float("nan")) == -1
     assert fwd_d(0.1, dtype=0) == -2                    # fp32 forward has no dropout
-    bwd_d = lib.fa_backward_dropout(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 100,
-                                    64, 0.125, 0, None, 2, 1.5, 1, 0, FAKE, 1 << 30, None)
-    assert bwd_d == -1
+    assert fwd_d(0.0, dtype=0, o_acc=FAKE) == -2        # nor an fp32 o_acc
+    assert fwd_d(0.1, o_acc=MISALIGNED) == -1
+
+    def bwd_d(p=0.1, o_acc=FAKE, dtype=2):
+        return lib.fa_backward_dropout(FAKE, FAKE, FAKE, o_acc, FAKE, FAKE, FAKE, FAKE, FAKE, 1,
+                                       2, 100, 64, 0.125, 0, None, dtype, p, 1, 0, FAKE, 1 << 30,
+                                       None)
+    assert bwd_d(p=1.5) == -1
+    assert bwd_d(o_acc=None) == -1                       # the fp32 O is required
+    assert bwd_d(o_acc=MISALIGNED) == -1
+    assert bwd_d(dtype=0) == -2
     assert lib.fa_dropout_mask(1, 1, 10, 0.5, 1, 0, None, None) == -1
     assert lib.fa_dropout_mask(1, 1, 10, 1.0, 1, 0, FAKE, None) == -1
     assert lib.fa_dropout_mask(1, 1, 70000, 0.5, 1, 0, FAKE, None) == -2
@@ -283,3 +306,25 @@ def test_forward_split_validation(lib):
     assert fsplit(lib, ws=MISALIGNED) == -3
     need = lib.fa_forward_split_workspace_size(1, 1, 4096, 64, 4)
     assert need > 0 and fsplit(lib, ws_bytes=need - 1) == -3
+
+
+def test_binding_rejects_host_or_mistyped_buffers():
+    """The Python binding checks every caller-supplied buffer before a call
+    reaches libfa: a host tensor, a wrong dtype or shape, or a non-contiguous
+    one raises ValueError (a host pointer handed to a kernel would fault)."""
+    import torch
+
+    from exact_io_aware_34_amd import fa
+    ok = torch.empty((2, 3, 4), dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU"):
+        fa._check_f32(ok, (2, 3, 4), "lse")                      # on the host
+    with pytest.raises(ValueError):
+        fa._check_workspace(torch.empty(16, dtype=torch.uint8))  # on the host
+    with pytest.raises(ValueError):
+        fa._check_f32(object(), (2, 3, 4), "grads")
+    assert fa._check_workspace(None) == 0
+    q = torch.empty((1, 1, 8, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        fa.forward(q, q, q)
+    with pytest.raises(ValueError, match="GPU"):
+        fa.backward(q, q, q, q, torch.empty((1, 1, 8)), q)

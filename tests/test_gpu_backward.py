@@ -122,7 +122,10 @@ def test_backward_row_statistics(fa, B, H, N, d, dtype, causal, sparse, dropout_
     scale = W.scale_for(d)
     qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
     md = None if mask is None else mask.cuda()
-    kw = dict(dropout_p=dropout_p, seed=7, offset=0) if dropout_p else {}
+    kw = {}
+    if dropout_p:
+        o_acc = torch.empty(qd.shape, dtype=torch.float32, device="cuda")
+        kw = dict(dropout_p=dropout_p, seed=7, offset=0, o_acc=o_acc)
     o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale, block_mask=md, **kw)
     ws = torch.full((fa.workspace_size(B, H, N, d),), 0xFF, dtype=torch.uint8, device="cuda")
     fa.backward(qd, kd, vd, o, lse, dod, causal=causal, scale=scale, block_mask=md,
@@ -132,7 +135,10 @@ def test_backward_row_statistics(fa, B, H, N, d, dtype, causal, sparse, dropout_
     second = (rows * 4 + 255) // 256 * 256
     neg_d = ws[:rows * 4].view(torch.float32).cpu().reshape(B, H, N)
     lse2 = ws[second:second + rows * 4].view(torch.float32).cpu().reshape(B, H, N)
-    ref_d = oracle.rowsum_do_o(f64(do), f64(o.cpu()))
+    # D is the row sum over the O the backward is given: the 16-bit o, or
+    # with dropout the forward's fp32 o_acc
+    given_o = o_acc if dropout_p else o
+    ref_d = oracle.rowsum_do_o(f64(do), f64(given_o.cpu()))
     assert_close("D", -f64(neg_d), ref_d, 1e-4 * max(1.0, float(np.abs(ref_d).max())))
     lse_c = lse.cpu()
     want = torch.where(torch.isneginf(lse_c), torch.full_like(lse_c, float("inf")),

@@ -4,17 +4,16 @@ fa_dropout_mask) through the C ABI, against the dropout oracle.
 * The keep mask is integer work: fa_dropout_mask must equal the oracle's
   Philox-4x32-10 mask bit for bit (several heads, ragged N, 64-bit seeds,
   offsets, p = 0).
-* Forward and backward with dropout against oracle.forward_head_dropout /
-  backward_head_dropout on the same inputs, seed and offset -- the backward's
-  inputs include the forward's stored 16-bit O, which the oracle receives as
-  well (with dropout O = c sum P v is not exact in 16 bits even for a one-key
-  row, where dS = P (c dP - D) cancels exactly: the D computed from the
-  stored O leaves its rounding there, up to 2e-2 on dQ at d = 128, which is
-  what the same-input comparison removes).  Every kept term is the
-  non-dropout term times c = 1 / (1 - p), so the tolerance is the 16-bit
-  path's times c.  A mask that differed from the oracle's in even a few
-  elements would show up far above it.
-* p = 0 takes the plain path and matches it exactly.
+* Forward then backward with dropout, end to end: the GPU forward's outputs
+  feed the GPU backward (which takes the forward's fp32 O for D), and every
+  element of o, lse, dq, dk, dv is compared with the oracle run from q, k, v,
+  dO, seed and offset alone, at the plain path's 16-bit bound (measured
+  worst: o 1.2e-2, dq 7.5e-3 against 1.5e-2 at bf16, d = 128, p = 0.2).  A
+  mask that differed from the oracle's in even a few elements would show up
+  far above it.
+* Causal row 0 sees one key, where dS = P (c Z dP - D) is exactly 0: its dQ
+  must vanish to fp32 rounding (the case that D from a 16-bit O broke).
+* p = 0 equals the plain path.
 """
 
 import numpy as np
@@ -85,14 +84,18 @@ def test_dropout_forward_backward(fa, B, H, N, d, dtype, causal, mask_kind, p):
     sc = W.scale_for(d)
     md = None if mask is None else mask.cuda()
     qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o_acc = torch.empty(qd.shape, dtype=torch.float32, device="cuda")
     o, lse = fa.forward(qd, kd, vd, causal=causal, scale=sc, block_mask=md, dropout_p=p,
-                        seed=seed, offset=offset)
+                        seed=seed, offset=offset, o_acc=o_acc)
     dq, dk, dv = fa.backward(qd, kd, vd, o, lse, dod, causal=causal, scale=sc, block_mask=md,
-                             dropout_p=p, seed=seed, offset=offset)
+                             dropout_p=p, seed=seed, offset=offset, o_acc=o_acc)
     torch.cuda.synchronize()
-    o, lse, dq, dk, dv = (t.cpu() for t in (o, lse, dq, dk, dv))
-    tol = TOL[DT[dtype]] * oracle.keep_scale(p)
+    o, lse, dq, dk, dv, o_acc = (t.cpu() for t in (o, lse, dq, dk, dv, o_acc))
+    # o is o_acc rounded to the input type
+    assert torch.equal(o, o_acc.to(o.dtype))
+    tol = TOL[DT[dtype]]
     mnp = None if mask is None else mask.numpy()
+    worst = {}
     for b in range(B):
         for h in range(H):
             a = [f64(t[b, h]) for t in (q, k, v, do)]
@@ -100,26 +103,51 @@ def test_dropout_forward_backward(fa, B, H, N, d, dtype, causal, mask_kind, p):
                                                  causal, mnp)
             assert_close(f"o[{b},{h}]", f64(o[b, h]), ro, tol)
             assert_close(f"lse[{b},{h}]", f64(lse[b, h]), rl, LSE_TOL)
+            assert_close(f"o_acc[{b},{h}]", f64(o_acc[b, h]), ro, tol)
             rq, rk, rv = oracle.backward_head_dropout(*a, sc, p, seed, offset, b * H + h, causal,
-                                                      mnp, o=f64(o[b, h]))
+                                                      mnp)
+            for name, got, ref in (("o", o, ro), ("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+                err = float(np.abs(f64(got[b, h]) - ref).max())
+                worst[name] = max(worst.get(name, 0.0), err)
             assert_close(f"dq[{b},{h}]", f64(dq[b, h]), rq, tol)
             assert_close(f"dk[{b},{h}]", f64(dk[b, h]), rk, tol)
             assert_close(f"dv[{b},{h}]", f64(dv[b, h]), rv, tol)
+    print(f"max abs err (bound {tol:.1e}):",
+          {k_: f"{e:.2e}" for k_, e in worst.items()}, flush=True)
+    if causal and mask_kind is None:
+        # row 0 sees key 0 only: dS_00 = 0 exactly, so dq[.., 0, :] ~ 0
+        assert dq[:, :, 0].abs().max().item() < 1e-5
     if mask_kind == "holed":
         assert torch.all(o[:, :, :128] == 0) and torch.all(torch.isneginf(lse[:, :, :128]))
 
 
 def test_dropout_p0_is_the_plain_path(fa):
+    """p = 0 keeps every element: the dropout kernels (run because o_acc is
+    asked for) give the plain forward's o and lse bit for bit, and a backward
+    that differs from the plain one only in D (from the fp32 O instead of the
+    16-bit one)."""
     q, k, v, do, _ = _inputs(1, 2, 200, 64, "bf16", None)
     qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
-    o0, l0 = fa.forward(qd, kd, vd, causal=True, dropout_p=0.0, seed=5)
+    o_acc = torch.empty(qd.shape, dtype=torch.float32, device="cuda")
+    o0, l0 = fa.forward(qd, kd, vd, causal=True, dropout_p=0.0, seed=5, o_acc=o_acc)
     o1, l1 = fa.forward(qd, kd, vd, causal=True)
-    g0 = fa.backward(qd, kd, vd, o0, l0, dod, causal=True, dropout_p=0.0, seed=5)
+    o2, l2 = fa.forward(qd, kd, vd, causal=True, dropout_p=0.0, seed=5)
+    g0 = fa.backward(qd, kd, vd, o0, l0, dod, causal=True, dropout_p=0.0, seed=5, o_acc=o_acc)
     g1 = fa.backward(qd, kd, vd, o1, l1, dod, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    assert torch.equal(o2, o1) and torch.equal(l2, l1)
+    assert torch.equal(o_acc.to(o0.dtype), o0)
     for a, b in zip(g0, g1):
-        assert torch.equal(a, b)
+        assert (a - b).abs().max().item() <= TOL[torch.bfloat16]
+
+
+def test_dropout_backward_needs_the_fp32_output(fa):
+    q, k, v, do, _ = _inputs(1, 1, 64, 64, "bf16", None)
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = fa.forward(qd, kd, vd, dropout_p=0.2, seed=1)
+    with pytest.raises(ValueError):
+        fa.backward(qd, kd, vd, o, lse, dod, dropout_p=0.2, seed=1)
 
 
 def test_dropout_changes_with_seed_and_offset(fa):

@@ -10,6 +10,8 @@
   bounds; p = 0 keeps everything; the mask depends on head, seed, offset.
 * forward_head_dropout: p = 0 is exact attention; pure-Python brute force
   with the mask; unbiased over many seeds.
+* philox(width=32) equals rocRAND's Philox-4x32-10 (its header compiled for the
+  CPU) on 406 counter/key tuples.
 * backward_head_dropout: central finite differences of sum(dO o O) with the
   mask fixed (dense and causal, p = 0.35 and 0.7); p = 0 is the plain
   backward.
@@ -17,6 +19,7 @@
 """
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -188,19 +191,52 @@ def test_backward_p0_is_plain_backward():
         np.testing.assert_allclose(a, b, atol=1e-13)
 
 
-def test_backward_takes_the_given_output():
+def test_backward_single_key_row_has_no_query_gradient():
+    """Causal row 0 sees one key: dS_00 = P_00 (c Z_00 dP_00 - D_0) with
+    D_0 = c Z_00 dP_00 exactly, so dQ_0 = 0 whatever the mask decided."""
     n, d, p = 20, 8, 0.3
     q, k, v, do = (RNG.standard_normal((n, d)) for _ in range(4))
-    o, _ = DR.forward_head_dropout(q, k, v, 0.3, p, 4, 0, 2, True)
-    a = DR.backward_head_dropout(q, k, v, do, 0.3, p, 4, 0, 2, True)
-    b = DR.backward_head_dropout(q, k, v, do, 0.3, p, 4, 0, 2, True, None, o)
-    for x, y in zip(a, b):
-        np.testing.assert_allclose(x, y, atol=1e-14)
-    # causal row 0 sees one key: dS_00 = c dP_00 - D_0 is exactly 0 with the
-    # exact O, and only an O that differs from it leaves dQ_0 non-zero.
-    assert np.abs(a[0][0]).max() < 1e-14
-    c = DR.backward_head_dropout(q, k, v, do, 0.3, p, 4, 0, 2, True, None, o * (1 + 1e-3))
-    assert np.abs(c[0][0]).max() > 1e-6 or not DR.keep_mask(2, [0], [0], 4, 0, p)[0, 0]
+    for seed in range(6):
+        dq, _, _ = DR.backward_head_dropout(q, k, v, do, 0.3, p, seed, 0, 2, True)
+        assert np.abs(dq[0]).max() < 1e-14
+
+
+def _rocrand_philox(tuples):
+    """rocRAND's Philox-4x32-10 round function (its header, built here with g++)."""
+    import shutil
+    import subprocess
+    import tempfile
+    src = os.path.join(os.path.dirname(__file__), "rocrand_philox_ref.cpp")
+    inc = "/opt/rocm/include"
+    if shutil.which("g++") is None or not os.path.exists(
+            os.path.join(inc, "rocrand", "rocrand_philox4x32_10.h")):
+        pytest.skip("g++ or the rocRAND headers are not installed")
+    with tempfile.TemporaryDirectory() as tmp:
+        exe = os.path.join(tmp, "philox_ref")
+        subprocess.run(["g++", "-O1", "-D__HIP_PLATFORM_AMD__", "-I", inc, src, "-o", exe],
+                       check=True, capture_output=True)
+        text = "".join(" ".join(str(int(x)) for x in t) + "\n" for t in tuples)
+        out = subprocess.run([exe], input=text, check=True, capture_output=True, text=True)
+    return [tuple(int(w) for w in line.split()) for line in out.stdout.splitlines()]
+
+
+def test_philox_4x32_matches_rocrand():
+    """philox(width=32) against rocRAND's Philox-4x32-10 (a library route):
+    its multipliers, Weyl constants, round function and word order."""
+    m = 0xFFFFFFFF
+    tuples = [(0, 0, 0, 0, 0, 0), (m, m, m, m, m, m), (1, 0, 0, 0, 0, 0), (0, 0, 0, 1, 0, 0),
+              (0, 0, 0, 0, 1, 0), (0, 0, 0, 0, 0, 1)]
+    tuples += [tuple(int(x) for x in RNG.integers(0, 2 ** 32, size=6, dtype=np.uint64))
+               for _ in range(400)]
+    ref = _rocrand_philox(tuples)
+    assert len(ref) == len(tuples)
+    for t, r in zip(tuples, ref):
+        assert DR.philox(t[:4], t[4:], width=32) == r
+    c = np.array([t[:4] for t in tuples], dtype=np.uint64).T
+    vec = DR.philox(tuple(c), (tuples[-1][4], tuples[-1][5]))
+    last = _rocrand_philox([tuple(int(c[w, i]) for w in range(4)) + tuples[-1][4:]
+                            for i in range(c.shape[1])])
+    assert [tuple(int(vec[w][i]) for w in range(4)) for i in range(c.shape[1])] == last
 
 
 # ---- planted slips ----

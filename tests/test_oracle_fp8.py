@@ -158,29 +158,23 @@ def test_rotation_reduces_error_with_outliers():
     assert min(ratios_o) > 1.0 and np.mean(ratios_o) > 1.1, ratios_o
 
 
-def test_fwht_f32_is_the_hadamard_product():
-    x = RNG.standard_normal((9, 128)).astype(np.float32)
-    np.testing.assert_allclose(F.fwht_f32(x), x.astype(np.float64) @ F.hadamard(128), rtol=0,
-                               atol=1e-4)
-    # small integers: every stage is exact, so the float32 result is exact
-    xi = RNG.integers(-8, 9, size=(5, 64)).astype(np.float32)
-    np.testing.assert_array_equal(F.fwht_f32(xi), xi @ F.hadamard(64))
-    e = np.zeros((1, 64), np.float32)
-    e[0, 5] = 1.0
-    np.testing.assert_array_equal(F.fwht_f32(e)[0], F.hadamard(64)[5])
-
-
-def test_prepare_f32_agrees_with_the_float64_method():
-    x = (RNG.standard_normal((130, 64)) * 3).astype(np.float32)
-    s = RNG.choice([-1.0, 1.0], 64)
-    c32, s32 = F.prepare_f32(x, s)
-    c64, s64 = F.block_quantize(F.rotate(x, s), 64)
-    np.testing.assert_allclose(s32, s64, rtol=1e-6)
-    assert np.mean(c32 != c64) < 2e-3                   # float32 vs float64 ties only
-    diff = c32 != c64
-    assert np.all(np.abs(c32[diff] - c64[diff]) <= 0.125 * np.abs(c64[diff]) + 2.0 ** -9)
-    c0, _ = F.prepare_f32(x, None)
-    np.testing.assert_array_equal(c0, F.block_quantize(x, 64)[0])
+def test_terms_recompose_the_output():
+    """The step-4 quantities returned with terms=True give back o and lse:
+    o = sv_max (e4m3(p r) @ v8) / l, lse = max_j s_ij + ln l (exp(s - m)
+    sums to l, and p is 1 at each row's max)."""
+    n, d = 150, 64
+    q, k, v = (RNG.standard_normal((n, d)) for _ in range(3))
+    s = RNG.choice([-1.0, 1.0], d)
+    o, l, t = F.fp8_forward_head(q, k, v, 0.125, True, None, s, terms=True)
+    o2 = t["sv_max"] * (F.e4m3(t["p"] * t["r"][None, :]) @ t["v8"]) / t["l"][:, None]
+    np.testing.assert_allclose(o2, o, rtol=0, atol=1e-14)
+    assert np.allclose(t["p"].max(axis=1), 1.0) and np.allclose(t["p"].sum(axis=1), t["l"])
+    assert np.all(np.triu(t["p"], 1) == 0)                      # causal: nothing above
+    assert t["r"].max() == 1.0 and np.all(t["r"] > 0)
+    # s_abs bounds |s| and equals it where every product has one sign
+    o3, l3, t3 = F.fp8_forward_head(np.abs(q), np.abs(k), v, 0.125, False, None, None,
+                                    terms=True)
+    np.testing.assert_allclose(t3["s_abs"].max(axis=1) + np.log(t3["l"]), l3, atol=1e-12)
 
 
 def test_rows_selects_query_rows():
