@@ -15,7 +15,8 @@ CSRC = os.path.join(HERE, "csrc")
 OBJDIR = os.path.join(HERE, "_build")
 LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "libfa.so")
-SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_dec.hip", "fa_fp8.hip", "fa_dropout.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_dec.hip", "fa_fp8.hip", "fa_dropout.hip",
+           "fa_noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU instructions are disabled for every device object.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

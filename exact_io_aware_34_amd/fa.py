@@ -62,6 +62,9 @@ _lib.fa_forward_splits.argtypes = [_i, _i, _i, _i, _i]
 _lib.fa_forward_splits.restype = _i
 _lib.fa_forward_split_workspace_size.argtypes = [_i, _i, _i, _i, _i]
 _lib.fa_forward_split_workspace_size.restype = ctypes.c_size_t
+_lib.fa_decode_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _i,
+                                   _vp]
+_lib.fa_decode_noalloc.restype = _i
 _lib.fa_status_string.argtypes = [_i]
 _lib.fa_status_string.restype = ctypes.c_char_p
 _lib.fa_abi_version.restype = _i
@@ -277,6 +280,38 @@ def decode(q, k, v, causal=False, scale=None, n_splits=0, out=None, lse=None, wo
     rc = _lib.fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, scale,
                         int(bool(causal)), int(n_splits), DTYPE_CODES[q.dtype], _ptr(workspace),
                         nbytes, _stream(stream))
+    if rc != 0:
+        raise FAError(rc)
+    return o, lse
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # FA_NOALLOC_SCRATCH_BYTES of fa.h
+
+
+def decode_noalloc(q, k, v, causal=False, scale=None, n_splits=0, out=None, lse=None,
+                   stream=None):
+    """decode() through fa_decode_noalloc: the key-range partials live in the
+    library's own device array, so the call allocates nothing on the device
+    (pass `out` and `lse` to allocate nothing here either).  Calls that
+    overlap on one GPU share that array and race."""
+    for t in (q, k, v):
+        if t.dim() != 4 or not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError("q, k, v must be contiguous 4-d GPU tensors of one dtype")
+    B, H, Nq, d = q.shape
+    if tuple(k.shape[:2]) != (B, H) or k.shape[3] != d or k.shape != v.shape:
+        raise ValueError("k and v must be (B, H, Nk, d) matching q")
+    if q.dtype not in DTYPE_CODES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    Nk = k.shape[2]
+    scale = default_scale(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous() or not o.is_cuda:
+        raise ValueError("out must be a contiguous GPU tensor shaped and typed like q")
+    _check_f32(lse, (B, H, Nq), "lse")
+    rc = _lib.fa_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
+                                scale, int(bool(causal)), int(n_splits), DTYPE_CODES[q.dtype],
+                                _stream(stream))
     if rc != 0:
         raise FAError(rc)
     return o, lse

@@ -231,6 +231,29 @@ int fa_decode_splits(int B, int H, int Nq, int Nk, int d, int n_splits);
 size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d, int n_splits);
 
 /*
+ * fa_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, results and errors as fa_decode, without the workspace:
+ * the key-range partials go to a device array of FA_NOALLOC_SCRATCH_BYTES
+ * (16 MiB) that the library holds on every GPU it runs on until the process
+ * ends.  The call allocates nothing (no hipMalloc, no library allocation);
+ * the first call on a device looks the array's address up once.  When the
+ * partials would need more than the array (fa_decode_workspace_size() of the
+ * same arguments > FA_NOALLOC_SCRATCH_BYTES; with the automatic range count
+ * that takes B * H * ranges * Nq * (d + 1) * 4 bytes, about 1.6 MB at
+ * B * H = 96, Nq = 16, d = 128) it returns FA_ERR_WORKSPACE and enqueues
+ * nothing.  Every call on one GPU shares that GPU's array and leaves its
+ * partials there: calls that overlap on one GPU (other streams, other host
+ * threads) race and must be ordered by the caller.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+int fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                      int n_splits, int dtype, void* stream);
+
+/*
  * FP8 forward with incoherent processing.
  *
  * FP8 attention is ruined by outliers unless the vectors are first rotated

@@ -62,7 +62,7 @@ def test_header_declares_the_boundary():
         "fa_decode_splits", "fa_decode_workspace_size", "fa_dropout_mask", "fa_forward",
         "fa_forward_dropout", "fa_forward_fp8", "fa_forward_fp8_workspace_size", "fa_fp8_prepare",
         "fa_backward_dropout", "fa_status_string", "fa_forward_split", "fa_forward_splits",
-        "fa_forward_split_workspace_size"])
+        "fa_forward_split_workspace_size", "fa_decode_noalloc"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -328,3 +328,21 @@ def test_binding_rejects_host_or_mistyped_buffers():
         fa.forward(q, q, q)
     with pytest.raises(ValueError, match="GPU"):
         fa.backward(q, q, q, q, torch.empty((1, 1, 8)), q)
+
+
+def test_decode_noalloc_validation(lib):
+    """fa_decode_noalloc rejects what fa_decode rejects, and partials larger
+    than its 16 MiB device array with FA_ERR_WORKSPACE, before touching the
+    GPU (these calls run without one)."""
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.fa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp]
+
+    def dn(B=1, H=32, Nq=16, Nk=64 * 128, d=128, n=64, dtype=2, q=FAKE):
+        return lib.fa_decode_noalloc(q, FAKE, FAKE, FAKE, FAKE, B, H, Nq, Nk, d, 0.088, 0, n,
+                                     dtype, None)
+    assert lib.fa_decode_workspace_size(1, 32, 16, 64 * 128, 128, 64) > (16 << 20)
+    assert dn() == -3
+    assert dn(q=None, n=1) == -1
+    assert dn(Nq=5, Nk=4, n=1) == -1
+    assert dn(d=96, n=1) == -2
+    assert dn(dtype=0, n=1) == -2
