@@ -66,8 +66,14 @@ def parse():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=12,
-                    help="heads of the workload the oracle is timed on")
+    ap.add_argument("--cpu-heads", type=int, default=0,
+                    help="heads of the workload the oracle is timed on "
+                         "(0: two per host core)")
+    ap.add_argument("--other-workloads", default="causal_b1h12_n23400_d64_f16,"
+                    "sparse_b2h16_n16384_d128_bf16",
+                    help="comma-separated workloads also timed (fwd + bwd) and reported "
+                         "in the `workloads` object; empty for none")
+    ap.add_argument("--other-steps", type=int, default=20)
     ap.add_argument("--decode-workload", default="decode_b8h12_q1_k65536_d64_bf16")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-cpu-heads", type=int, default=24)
@@ -117,39 +123,66 @@ def flops(w, mask):
     return 4.0 * f, 10.0 * f
 
 
-def cpu_baseline(w, inputs, n_heads):
-    """Time the fp64 oracle on `n_heads` heads of the same workload.
-
-    The forward and the backward are timed separately; `value` is their
-    combined FLOPs over their combined time (the same ratio as the GPU step).
-    """
-    from threadpoolctl import threadpool_info
+def _cpu_pool_run(fn, jobs, procs):
+    """Run fn(*job) for every job over `procs` spawned worker processes (one
+    BLAS thread each; they import only numpy and the oracle).  The workers
+    are started and warmed before the clock starts.  Returns wall seconds."""
+    import concurrent.futures
+    import multiprocessing
 
     import oracle
+    saved = {k: os.environ.get(k) for k in ("OPENBLAS_NUM_THREADS", "OMP_NUM_THREADS")}
+    for k in saved:
+        os.environ[k] = "1"
+    try:
+        with concurrent.futures.ProcessPoolExecutor(
+                procs, mp_context=multiprocessing.get_context("spawn")) as ex:
+            import numpy as np
+            tiny = np.ones((2, 8))
+            list(ex.map(oracle.rowsum_do_o, [tiny] * (4 * procs), [tiny] * (4 * procs)))
+            t0 = time.perf_counter()
+            for f in [ex.submit(fn, *job) for job in jobs]:
+                f.result()
+            return time.perf_counter() - t0
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+def cpu_baseline(w, inputs, n_heads=None):
+    """Time the fp64 oracle on a sample of heads of the same workload, the
+    heads spread over os.cpu_count() processes with one BLAS thread each.
+
+    All sampled heads' forwards run as one batch of jobs, then all their
+    backwards; `value` is their combined FLOPs over the combined wall time
+    (the same ratio as the GPU step).
+    """
+    import oracle
+    procs = max(1, os.cpu_count() or 1)
+    n = min(w.B * w.H, n_heads or 2 * procs)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)][:n]
     mask = None if inputs["mask"] is None else inputs["mask"].numpy()
-    heads = [(b, h) for b in range(w.B) for h in range(w.H)][:n_heads]
-    t_fwd = t_bwd = 0.0
+    fwd_jobs, bwd_jobs = [], []
     for b, h in heads:
-        a = [inputs[n][b, h].double().numpy() for n in ("q", "k", "v")]
-        t0 = time.perf_counter()
-        oracle.forward_head(*a, w.scale, causal=w.causal, block_mask=mask)
-        t1 = time.perf_counter()
+        a = [inputs[x][b, h].float().numpy() for x in ("q", "k", "v")]
+        fwd_jobs.append((*a, w.scale, w.causal, mask))
         if w.backward:
-            oracle.backward_head(*a, inputs["do"][b, h].double().numpy(), w.scale,
-                                 causal=w.causal, block_mask=mask)
-        t_fwd += t1 - t0
-        t_bwd += time.perf_counter() - t1
+            bwd_jobs.append((*a, inputs["do"][b, h].float().numpy(), w.scale, w.causal, mask))
+    procs = min(procs, len(heads))
+    t_fwd = _cpu_pool_run(oracle.forward_head, fwd_jobs, procs)
+    t_bwd = _cpu_pool_run(oracle.backward_head, bwd_jobs, procs) if w.backward else 0.0
     f_fwd, f_bwd = flops(w, inputs["mask"])
     per_head_fwd = f_fwd / (w.B * w.H)
     per_head_bwd = (f_bwd if w.backward else 0.0) / (w.B * w.H)
-    n = len(heads)
-    threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
     out = {"value": (per_head_fwd + per_head_bwd) * n / (t_fwd + t_bwd) / 1e12, "unit": "TFLOPS",
-           "cores": threads, "kind": "oracle", "seconds": round(t_fwd + t_bwd, 3),
+           "cores": procs, "kind": "oracle", "seconds": round(t_fwd + t_bwd, 3),
            "fwd_tflops": per_head_fwd * n / t_fwd / 1e12, "fwd_seconds": round(t_fwd, 3),
            "sample": f"{n} of {w.B * w.H} heads, forward"
                      f"{' + backward' if w.backward else ''}, numpy float64, "
-                     f"os.cpu_count()={os.cpu_count()}"}
+                     f"{procs} processes x 1 BLAS thread, os.cpu_count()={os.cpu_count()}"}
     if w.backward:
         out["bwd_tflops"] = per_head_bwd * n / t_bwd / 1e12
         out["bwd_seconds"] = round(t_bwd, 3)
@@ -399,6 +432,87 @@ def bench_dropout(fa, w, tensors, mask, steps, warmup, p, plain_ms):
     return out
 
 
+def pass_summary(w, mask_cpu, fwd_ms, bwd_ms, wall, steps):
+    """Per-pass times, TFLOP/s, fractions of peak and the roofline of the
+    dominant call (the backward when present: its kernels run back to back
+    on the stream and are timed together; else the forward kernel)."""
+    mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
+    f_fwd, f_bwd = flops(w, mask_cpu)
+    if not w.backward:
+        f_bwd = 0.0
+    ms_step = wall * 1e3 / steps
+    peak = PEAK_TFLOPS[w.dtype]
+    fwd_tf = f_fwd / (mean(fwd_ms) * 1e-3) / 1e12
+    bwd_tf = f_bwd / (mean(bwd_ms) * 1e-3) / 1e12 if w.backward else None
+    if w.backward and mean(bwd_ms) >= mean(fwd_ms):
+        dom, dom_key, dom_ms, dom_flops = ("fa_backward (bwd_dq + bwd_dkdv)", "backward",
+                                           mean(bwd_ms), f_bwd)
+    else:
+        dom, dom_key, dom_ms, dom_flops = "fa_forward (fwd kernel)", "forward", mean(fwd_ms), f_fwd
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    rec = recorded_traffic(w.name)
+    traffic = None if rec is None else rec["bytes_per_call"].get(dom_key)
+    return {
+        "value": round((f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12, 2),
+        "ms_per_step": round(ms_step, 4),
+        "fwd_ms": round(mean(fwd_ms), 4), "bwd_ms": round(mean(bwd_ms), 4),
+        "fwd_ms_median_min": [round(statistics.median(fwd_ms), 4), round(min(fwd_ms), 4)],
+        "bwd_ms_median_min": [round(statistics.median(bwd_ms), 4), round(min(bwd_ms), 4)],
+        "fwd_tflops": round(fwd_tf, 2), "fwd_frac_peak": round(fwd_tf / peak, 4),
+        "bwd_tflops": None if bwd_tf is None else round(bwd_tf, 2),
+        "bwd_frac_peak": None if bwd_tf is None else round(bwd_tf / peak, 4),
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic, "avg_ms": round(dom_ms, 4)},
+    }
+
+
+def skip_efficiency(fa, w, tensors, mask, steps, fwd_ms, bwd_ms):
+    """(T_dense / T_sparse) / (1 / kept fraction), the dense time from the
+    same kernels with no mask."""
+    mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
+    d_fwd, d_bwd, _ = time_passes(fa, w, tensors, None, max(3, steps // 2), 2)
+    kept = float(mask.float().mean())
+    return {"kept_tile_fraction": round(kept, 5),
+            "fwd": round(mean(d_fwd) / mean(fwd_ms) * kept, 4),
+            "bwd": round(mean(d_bwd) / mean(bwd_ms) * kept, 4) if w.backward else None,
+            "dense_fwd_ms": round(mean(d_fwd), 4),
+            "dense_bwd_ms": round(mean(d_bwd), 4) if w.backward else None}
+
+
+def workload_tensors(fa, w, inputs, dev):
+    import torch
+    q, k, v = (inputs[n].to(dev) for n in ("q", "k", "v"))
+    do = inputs["do"].to(dev) if w.backward else None
+    mask = None if inputs["mask"] is None else inputs["mask"].to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    grads = tuple(torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
+                  for _ in range(3)) if w.backward else None
+    ws = torch.empty(max(1, fa.workspace_size(w.B, w.H, w.N, w.d)), dtype=torch.uint8, device=dev)
+    return (q, k, v, do, o, lse, ws, grads), mask
+
+
+def bench_other(fa, name, steps, warmup):
+    """Forward + backward of another workload: the same fields as the line."""
+    import torch
+
+    from exact_io_aware_34_amd import workloads as W
+    w = W.WORKLOADS[name]
+    inputs = W.make(name)
+    tensors, mask = workload_tensors(fa, w, inputs, torch.device("cuda:0"))
+    fwd_ms, bwd_ms, wall = time_passes(fa, w, tensors, mask, steps, warmup)
+    out = {"B": w.B, "H": w.H, "N": w.N, "d": w.d, "dtype": w.dtype, "causal": w.causal,
+           "block_sparse": w.sparse, "steps": steps, "warmup": warmup,
+           "work_fraction": round(work_fraction(w, inputs["mask"]), 5)}
+    out.update(pass_summary(w, inputs["mask"], fwd_ms, bwd_ms, wall, steps))
+    if w.sparse:
+        out["skip_efficiency"] = skip_efficiency(fa, w, tensors, mask, steps, fwd_ms, bwd_ms)
+    del tensors, mask
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -418,74 +532,31 @@ def main():
     w = W.WORKLOADS[name]
     inputs = W.make(name)
     dev = torch.device("cuda:0")
-    q, k, v = (inputs[n].to(dev) for n in ("q", "k", "v"))
-    do = inputs["do"].to(dev) if w.backward else None
-    mask = None if inputs["mask"] is None else inputs["mask"].to(dev)
     B, H, N, d = w.B, w.H, w.N, w.d
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    grads = tuple(torch.empty((B, H, N, d), dtype=torch.float32, device=dev) for _ in range(3))
-    ws = torch.empty(fa.workspace_size(B, H, N, d), dtype=torch.uint8, device=dev)
+    tensors, mask = workload_tensors(fa, w, inputs, dev)
     if args.calibrate_copy:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    tensors = (q, k, v, do, o, lse, ws, grads)
     fwd_ms, bwd_ms, wall = time_passes(fa, w, tensors, mask, args.steps, args.warmup)
 
     mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
-    f_fwd, f_bwd = flops(w, mask.cpu() if mask is not None else None)
-    if not w.backward:
-        f_bwd = 0.0
-    ms_step = wall * 1e3 / args.steps
-    value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[w.dtype]
-    fwd_tf = f_fwd / (mean(fwd_ms) * 1e-3) / 1e12
-    bwd_tf = f_bwd / (mean(bwd_ms) * 1e-3) / 1e12 if w.backward else None
-
-    # Dominant work by time: the backward call (its kernels run back to back
-    # on the stream, timed together) when present, else the forward kernel.
-    if w.backward and mean(bwd_ms) >= mean(fwd_ms):
-        dom, dom_key, dom_ms, dom_flops = ("fa_backward (bwd_dq + bwd_dkdv)", "backward",
-                                           mean(bwd_ms), f_bwd)
-    else:
-        dom, dom_key, dom_ms, dom_flops = "fa_forward (fwd kernel)", "forward", mean(fwd_ms), f_fwd
-    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
-    rec = recorded_traffic(name)
-    traffic = None if rec is None else rec["bytes_per_call"].get(dom_key)
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
-                "avg_ms": round(dom_ms, 4)}
-
+    summary = pass_summary(w, inputs["mask"], fwd_ms, bwd_ms, wall, args.steps)
+    ms_step = summary["ms_per_step"]
     out = {
         "metric": METRIC if name == W.HEADLINE else f"attention TFLOPS ({name})",
-        "value": round(value, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "value": summary["value"], "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
                    "block_sparse": w.sparse, "passes": "fwd+bwd" if w.backward else "fwd",
                    "work_fraction": round(work_fraction(w, inputs["mask"]), 5)},
-        "fwd_ms": round(mean(fwd_ms), 4), "bwd_ms": round(mean(bwd_ms), 4),
-        "fwd_ms_median_min": [round(statistics.median(fwd_ms), 4), round(min(fwd_ms), 4)],
-        "bwd_ms_median_min": [round(statistics.median(bwd_ms), 4), round(min(bwd_ms), 4)],
-        "fwd_tflops": round(fwd_tf, 2), "fwd_frac_peak": round(fwd_tf / peak, 4),
-        "bwd_tflops": None if bwd_tf is None else round(bwd_tf, 2),
-        "bwd_frac_peak": None if bwd_tf is None else round(bwd_tf / peak, 4),
-        "roofline": roofline,
     }
+    out.update({k_: v_ for k_, v_ in summary.items() if k_ not in ("value", "ms_per_step")})
     if w.sparse:
-        # Skip efficiency: (T_dense / T_sparse) / (1 / kept fraction), the
-        # dense time from the same kernels with no mask.
-        d_fwd, d_bwd, _ = time_passes(fa, w, tensors, None, max(3, args.steps // 2), 2)
-        kept = float(mask.float().mean())
-        out["skip_efficiency"] = {
-            "kept_tile_fraction": round(kept, 5),
-            "fwd": round(mean(d_fwd) / mean(fwd_ms) * kept, 4),
-            "bwd": round(mean(d_bwd) / mean(bwd_ms) * kept, 4) if w.backward else None,
-            "dense_fwd_ms": round(mean(d_fwd), 4),
-            "dense_bwd_ms": round(mean(d_bwd), 4) if w.backward else None}
+        out["skip_efficiency"] = skip_efficiency(fa, w, tensors, mask, args.steps, fwd_ms, bwd_ms)
     if fa.forward_splits(B, H, N, d, 0) > 1:
         out["split_forward"] = bench_split(fa, w, tensors, mask, args.steps, args.warmup,
                                            mean(fwd_ms))
@@ -499,8 +570,14 @@ def main():
     if not args.no_decode:
         out["decode"] = bench_decode(fa, args.decode_workload, args.steps, args.warmup,
                                      args.decode_cpu_heads, not args.no_cpu_baseline)
+    others = [x for x in args.other_workloads.split(",") if x and x != name]
+    if others:
+        del tensors, mask
+        torch.cuda.empty_cache()
+        out["workloads"] = {x: bench_other(fa, x, args.other_steps, max(5, args.other_steps // 2))
+                            for x in others}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_heads)
+        out["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_heads or None)
     print(json.dumps(out))
 
 

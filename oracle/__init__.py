@@ -43,6 +43,7 @@ from .attention import (  # noqa: F401
     forward_head,
     backward,
     backward_head,
+    backward_head_sampled,
     rowsum_do_o,
 )
 from .decode import (  # noqa: F401

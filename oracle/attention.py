@@ -121,6 +121,45 @@ def backward_head(q, k, v, do, scale, causal=False, block_mask=None,
     return dq, dk, dv
 
 
+def backward_head_sampled(q, k, v, do, scale, causal=False, block_mask=None, q_rows=(),
+                          k_cols=(), mask_block=MASK_BLOCK, chunk=512):
+    """One head's dq at query rows `q_rows` and dk, dv at key rows `k_cols`.
+
+    The same definitions as backward_head, evaluated only where asked:
+    dq_i = scale sum_j dS_ij k_j needs row i alone; dk_j = scale sum_i dS_ij q_i
+    and dv_j = sum_i P_ij dO_i need P_ij and D_i = sum_c dO_ic o_ic of every
+    row i that sees key j, so every such row is evaluated whole (its softmax
+    and its output o_i), in chunks of rows; chunks that hold no sampled row
+    and see none of the sampled keys are passed over.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    n = k.shape[0]
+    q_rows = np.asarray(q_rows, dtype=np.int64)
+    k_cols = np.asarray(k_cols, dtype=np.int64)
+    dq = np.zeros((q_rows.size, q.shape[1]))
+    dk = np.zeros((k_cols.size, k.shape[1]))
+    dv = np.zeros((k_cols.size, v.shape[1]))
+    for c0 in range(0, n, chunk):
+        r = np.arange(c0, min(n, c0 + chunk))
+        ok = allowed(r, n, causal, block_mask, mask_block)
+        in_chunk = (q_rows >= c0) & (q_rows < c0 + r.size)
+        sees = ok[:, k_cols]
+        if not in_chunk.any() and not sees.any():
+            continue
+        s = scale * (q[r] @ k.T)
+        p, _ = _row_softmax(s, ok)
+        d_row = rowsum_do_o(do[r], p @ v)
+        if in_chunk.any():
+            li = q_rows[in_chunk] - c0
+            ds = p[li] * (do[r][li] @ v.T - d_row[li, None])
+            dq[in_chunk] = scale * (ds @ k)
+        pc = p[:, k_cols]
+        ds_c = pc * (do[r] @ v[k_cols].T - d_row[:, None])
+        dv += pc.T @ do[r]
+        dk += scale * (ds_c.T @ q[r])
+    return dq, dk, dv
+
+
 def _heads(x):
     x = np.asarray(x)
     return x.shape[0], x.shape[1]

@@ -5,6 +5,10 @@ same rounded inputs: O, dQ, dK, dV within 1e-5 (fp32 inputs), 5e-3 (fp16) or
 1.5e-2 (bf16); lse within 1e-3.
 """
 
+import concurrent.futures
+import multiprocessing
+import os
+
 import numpy as np
 import torch
 
@@ -67,3 +71,39 @@ def random_block_mask(n, frac, seed, keep_diagonal=True):
     if keep_diagonal:
         m |= torch.eye(t, dtype=torch.bool)
     return m.to(torch.uint8)
+
+
+def sample_rows(n, count, seed, must=()):
+    """Sorted distinct row indices: `must` (clipped to the range) plus random ones."""
+    g = np.random.default_rng(seed)
+    picks = set(int(x) for x in must if 0 <= x < n)
+    while len(picks) < min(n, count):
+        picks.add(int(g.integers(0, n)))
+    return np.array(sorted(picks), dtype=np.int64)
+
+
+def oracle_backward_sampled(q, k, v, do, scale, causal, mask, samples, workers=16):
+    """oracle.backward_head_sampled for many heads at once, spread over up to
+    `workers` processes (spawned, one BLAS thread each; they import only numpy
+    and the oracle).  samples: {(b, h): (q_rows, k_cols)}.  Returns
+    {(b, h): (dq_rows, dk_cols, dv_cols)}."""
+    m = mask_np(mask)
+    n_workers = max(1, min(workers, os.cpu_count() or 1, len(samples)))
+    saved = {key: os.environ.get(key) for key in ("OPENBLAS_NUM_THREADS", "OMP_NUM_THREADS")}
+    for key in saved:
+        os.environ[key] = "1"
+    try:
+        with concurrent.futures.ProcessPoolExecutor(
+                n_workers, mp_context=multiprocessing.get_context("spawn")) as ex:
+            futs = {}
+            for (b, h), (rows, cols) in samples.items():
+                args = [t[b, h].float().numpy() for t in (q, k, v, do)]
+                futs[(b, h)] = ex.submit(oracle.backward_head_sampled, *args, scale, causal, m,
+                                         rows, cols)
+            return {key: f.result() for key, f in futs.items()}
+    finally:
+        for key, val in saved.items():
+            if val is None:
+                os.environ.pop(key, None)
+            else:
+                os.environ[key] = val

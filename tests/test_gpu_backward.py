@@ -2,8 +2,10 @@
 
 The GPU backward consumes the GPU forward's O and lse (as a caller would);
 the oracle recomputes everything from the same rounded inputs.  Full-size
-workloads are compared on whole heads the oracle can afford, and on
-invariants that hold for every head at any size.
+workloads are compared element by element on whole heads the oracle can
+afford, on sampled dQ rows and dK/dV key rows of every head (each sampled
+key needs every row that sees it evaluated whole, spread over worker
+processes), and on invariants that hold for every head at any size.
 """
 
 import numpy as np
@@ -12,7 +14,7 @@ import torch
 
 from exact_io_aware_34_amd import workloads as W
 from tests.parity import (DT, TOL, assert_close, f64, oracle_backward_heads,
-                          random_block_mask)
+                          oracle_backward_sampled, random_block_mask, sample_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -86,6 +88,26 @@ def test_backward_named_large_workloads(fa, name):
         assert_close(f"dq[{b},{h}]", f64(dq[b, h]), rq, tol)
         assert_close(f"dk[{b},{h}]", f64(dk[b, h]), rk, tol)
         assert_close(f"dv[{b},{h}]", f64(dv[b, h]), rv, tol)
+    # Every head, sampled: 8 dQ rows and 8 dK/dV key rows (the first and last
+    # rows, tile edges, random ones), element by element.
+    N = wl.N
+    samples = {}
+    for b in range(wl.B):
+        for h in range(wl.H):
+            i = b * wl.H + h
+            samples[(b, h)] = (sample_rows(N, 8, 1000 + i, must=(0, N - 1, 127 + 128 * i)),
+                               sample_rows(N, 8, 2000 + i, must=(0, N - 1, 128 * i + 64)))
+    ref = oracle_backward_sampled(w["q"], w["k"], w["v"], w["do"], w["scale"], w["causal"],
+                                  w["mask"], samples)
+    worst = [0.0, 0.0, 0.0]
+    for (b, h), (rows, cols) in samples.items():
+        rq, rk, rv = ref[(b, h)]
+        for j, (what, got, r, idx) in enumerate((("dq", dq, rq, rows), ("dk", dk, rk, cols),
+                                                 ("dv", dv, rv, cols))):
+            worst[j] = max(worst[j], assert_close(f"{what}[{b},{h}] sampled",
+                                                  f64(got[b, h, idx]), r, tol))
+    print(f"{name}: every head sampled, max abs err dq {worst[0]:.2e} dk {worst[1]:.2e} "
+          f"dv {worst[2]:.2e} (bound {tol:.1e})", flush=True)
     # Invariants on every head: sum_j dK_j = 0 (rows of dS sum to zero) and
     # sum_j dV_j = sum_i dO_i (rows of P sum to one; every row sees a key).
     do64 = w["do"].double()

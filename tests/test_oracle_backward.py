@@ -148,3 +148,41 @@ def test_batched_wrapper_matches_heads():
             gh = backward_head(q[b, h], k[b, h], v[b, h], do[b, h], 0.3, True)
             for x, y in zip(g, gh):
                 np.testing.assert_array_equal(x[b, h], y)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("masked", [False, True])
+@pytest.mark.parametrize("chunk", [7, 64, 500])
+def test_sampled_gradients_match_torch_autograd_fp64(causal, masked, chunk):
+    """backward_head_sampled at sampled query rows and key columns against
+    torch autograd through its attention routine (an independent route),
+    including chunks that hold no sampled row and see no sampled key."""
+    n, d, mb = 200, 16, 32
+    q, k, v, do = randn(n, d), randn(n, d), randn(n, d), randn(n, d)
+    bm = None
+    if masked:
+        bm = (np.random.default_rng(9).random((7, 7)) < 0.3).astype(np.uint8)
+        np.fill_diagonal(bm, 1)
+    rows = np.array([0, 1, 63, 64, 150, 199])
+    cols = np.array([0, 5, 31, 32, 130, 199])
+    dq, dk, dv = oracle.backward_head_sampled(q, k, v, do, 0.3, causal, bm, rows, cols, mb,
+                                              chunk=chunk)
+    ok = torch.from_numpy(oracle.allowed(np.arange(n), n, causal, bm, mb))
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_() for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq[None], tk[None], tv[None], attn_mask=ok[None], scale=0.3)[0]
+    o.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(dq, tq.grad.numpy()[rows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy()[cols], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy()[cols], rtol=0, atol=1e-12)
+
+
+def test_sampled_gradients_finite_differences():
+    n, d = 12, 8
+    q, k, v, do = randn(n, d), randn(n, d), randn(n, d), randn(n, d)
+    rows, cols = np.array([0, 7, 11]), np.array([2, 11])
+    dq, dk, dv = oracle.backward_head_sampled(q, k, v, do, 0.35, True, None, rows, cols, 4,
+                                              chunk=5)
+    fq, fk, fv = finite_difference_grads(q, k, v, do, 0.35, True, None, 4)
+    for got, ref in ((dq, fq[rows]), (dk, fk[cols]), (dv, fv[cols])):
+        assert np.max(np.abs(got - ref)) <= 1e-6 * max(1e-12, np.max(np.abs(ref)))
