@@ -34,6 +34,11 @@ size_t delta_bytes(int B, int H, int N) {
   return (b + 255) / 256 * 256;
 }
 
+size_t order_bytes(int N) {
+  const size_t b = 2 * (size_t)((N + 127) / 128) * sizeof(int);
+  return (b + 255) / 256 * 256;
+}
+
 // Decode key ranges.  With n_splits = 0 the count aims at about 192
 // (b*h, range) workgroups -- one workgroup on each of three quarters of the
 // 256 CUs -- with ranges no shorter than 512 keys.  Measured on the decode
@@ -314,7 +319,9 @@ int fa_forward_split(const void* q, const void* k, const void* v, void* o, float
 
 size_t fa_backward_workspace_size(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
-  return 2 * delta_bytes(B, H, N);  // -D and the log2-domain lse, one fp32 each per row
+  // -D and the log2-domain lse, one fp32 each per row; then the block-sparse
+  // work order, two int32 per 128-row tile.
+  return 2 * delta_bytes(B, H, N) + order_bytes(N);
 }
 
 int fa_backward(const void* q, const void* k, const void* v, const void* o,
@@ -386,6 +393,8 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
   p.dv = dv;
   p.neg_delta = (float*)workspace;
   p.lse2 = (float*)((char*)workspace + delta_bytes(B, H, N));
+  p.qt_order = (int*)((char*)workspace + 2 * delta_bytes(B, H, N));
+  p.kt_order = p.qt_order + (N + 127) / 128;
   p.mask = block_mask;
   p.BH = B * H;
   p.N = N;

@@ -84,7 +84,13 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdPara
   const int N = p.N;
   const int n_kt = (N + BC - 1) / BC;
   int bh, j;
-  if (CAUSAL) {
+  if (SPARSE) {
+    // Heads in XCD-aware runs as below; within a head, key tiles with the
+    // most visible query tiles first (the order of sparse_order_kernel).
+    const int lid = xcd_remap(blockIdx.x, n_kt * p.BH);
+    bh = lid / n_kt;
+    j = p.kt_order[lid - bh * n_kt];
+  } else if (CAUSAL) {
     // Key tiles with the most query tiles (small j) first across all heads.
     bh = blockIdx.x % p.BH;
     j = blockIdx.x / p.BH;
@@ -403,7 +409,13 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dq_u_kernel(BwdParams
   const int N = p.N;
   const int n_qt = (N + BR - 1) / BR;
   int bh, qt;
-  if (CAUSAL) {
+  if (SPARSE) {
+    // Heads in XCD-aware runs; within a head, query tiles with the most
+    // visible key tiles first (sparse_order_kernel).
+    const int lid = xcd_remap(blockIdx.x, n_qt * p.BH);
+    bh = lid / n_qt;
+    qt = p.qt_order[lid - bh * n_qt];
+  } else if (CAUSAL) {
     bh = blockIdx.x % p.BH;
     qt = n_qt - 1 - blockIdx.x / p.BH;
   } else {
@@ -674,11 +686,49 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dq_u_kernel(BwdParams
   }
 }
 
+// Block-sparse work order: the mask's 128-row tiles (query tiles) and
+// 128-column tiles (key tiles) sorted by how many visible tiles each holds,
+// most first, ties by index (with the causal flag only tiles on or below the
+// diagonal count).  The backward kernels take their tiles in this order, so
+// the longest workgroups start first and the shortest fill the tail.  One
+// workgroup; counts and ranks in LDS (n <= FWD_MAX_MASK_TILES).
+__global__ __launch_bounds__(1024) void sparse_order_kernel(const uint8_t* __restrict__ mask, int n,
+                                                            int causal, int* __restrict__ qt_order,
+                                                            int* __restrict__ kt_order) {
+  __shared__ int row_n[FWD_MAX_MASK_TILES], col_n[FWD_MAX_MASK_TILES];
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    int rc = 0, cc = 0;
+    for (int t = 0; t < n; ++t) {
+      rc += (mask[(size_t)i * n + t] != 0) && (!causal || t <= i);
+      cc += (mask[(size_t)t * n + i] != 0) && (!causal || t >= i);
+    }
+    row_n[i] = rc;
+    col_n[i] = cc;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int ri = row_n[i], ci = col_n[i];
+    int rr = 0, cr = 0;
+    for (int t = 0; t < n; ++t) {
+      rr += row_n[t] > ri || (row_n[t] == ri && t < i);
+      cr += col_n[t] > ci || (col_n[t] == ci && t < i);
+    }
+    qt_order[rr] = i;
+    kt_order[cr] = i;
+  }
+}
+
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
   // The dQ kernel also writes the row statistics (-D, lse * log2 e) that the
   // dK/dV kernel reads, so it runs first.
   const dim3 grid(((p.N + 127) / 128) * p.BH), block(256);
+  if constexpr (SPARSE) {
+    sparse_order_kernel<<<1, 1024, 0, st>>>(p.mask, p.mask_tiles, CAUSAL ? 1 : 0, p.qt_order,
+                                             p.kt_order);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   bwd_dq_u_kernel<T, D, CAUSAL, SPARSE, DROP><<<grid, block, 0, st>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

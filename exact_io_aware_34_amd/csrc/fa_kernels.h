@@ -74,6 +74,8 @@ struct BwdParams {
   float* dv;
   float* neg_delta;  // workspace: -D_i = -sum_c dO_ic o_ic, (B*H, N)
   float* lse2;   // workspace: lse_i * log2(e), +inf for rows with no visible key
+  int* qt_order;  // workspace (block-sparse): query tiles, most visible key tiles first
+  int* kt_order;  // workspace (block-sparse): key tiles, most visible query tiles first
   const uint8_t* mask;
   int BH, N;
   int n_ktiles, n_qtiles, mask_tiles;

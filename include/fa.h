@@ -112,7 +112,8 @@ int fa_forward_splits(int B, int H, int N, int d, int n_splits);
 size_t fa_forward_split_workspace_size(int B, int H, int N, int d, int n_splits);
 
 /* Bytes of device workspace fa_backward needs for this shape (0 on bad input):
- * two fp32 values per (b, h, row), each array padded to 256 bytes. */
+ * two fp32 values per (b, h, row), each array padded to 256 bytes, then two
+ * int32 per 128-row tile (the block-sparse work order), padded to 256 bytes. */
 size_t fa_backward_workspace_size(int B, int H, int N, int d);
 
 /*

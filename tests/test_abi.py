@@ -79,8 +79,11 @@ def test_status_strings(lib):
 
 
 def test_workspace_size(lib):
-    assert lib.fa_backward_workspace_size(4, 12, 8192, 64) == 2 * 4 * 12 * 8192 * 4
-    assert lib.fa_backward_workspace_size(1, 1, 3, 64) == 512
+    # -D and lse * log2 e (fp32 per row, each padded to 256 bytes), then the
+    # block-sparse order (two int32 per 128-row tile, padded to 256 bytes)
+    assert lib.fa_backward_workspace_size(4, 12, 8192, 64) == 2 * 4 * 12 * 8192 * 4 + 512
+    assert lib.fa_backward_workspace_size(1, 1, 3, 64) == 3 * 256
+    assert lib.fa_backward_workspace_size(1, 1, 2048 * 128, 64) == 2 * 2048 * 128 * 4 + 16384
     assert lib.fa_backward_workspace_size(0, 1, 3, 64) == 0
 
 
@@ -120,7 +123,9 @@ def test_backward_validation(lib):
     assert bwd(lib, d=80) == -2
     assert bwd(lib, dtype=0) == -2                      # fp32 backward not built
     assert bwd(lib, ws=None) == -3
-    assert bwd(lib, ws_bytes=2 * 2 * 3 * 100 * 4 - 1) == -3
+    need = lib.fa_backward_workspace_size(2, 3, 100, 64)
+    assert need == 2 * 2560 + 256
+    assert bwd(lib, ws_bytes=need - 1) == -3
 
 
 def test_block_mask_size_limit(lib):
