@@ -40,13 +40,12 @@ namespace {
 template <int V>
 using ic = std::integral_constant<int, V>;
 
-template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
-__global__ __launch_bounds__(256, fwd16_waves(D)) void fwd16_kernel(FwdParams p) {
+template <typename T, int D, int NS, bool CAUSAL, bool SPARSE, bool DROP>
+__global__ __launch_bounds__(256, fwd16_waves(D, NS)) void fwd16_kernel(FwdParams p) {
   using VT = typename V8<T>::t;
   using HT = typename V8<T>::h;
   constexpr int NW = 4, BR = 128;              // 4 waves x 32 query rows
   constexpr int BC = 64;                       // keys per K/V tile (two 32-key units)
-  constexpr int NS = fwd16_slots(D);           // slots per ring
   constexpr int DS = D / 16, DB = D / 32, CPR = D / 8;
   constexpr int TILE = BC * D;                 // elements of one K (or V) tile
   constexpr int DMA_N = BC * CPR / 256;        // copies per wave per tile
@@ -573,19 +572,30 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(FwdParams p) {
   }
 }
 
+template <typename T, int D, int NS, bool DROP>
+hipError_t launch16_v(const FwdParams& p, bool causal, bool sparse, dim3 grid, hipStream_t st) {
+  const dim3 block(256);
+  if (causal && sparse) fwd16_kernel<T, D, NS, true, true, DROP><<<grid, block, 0, st>>>(p);
+  else if (causal) fwd16_kernel<T, D, NS, true, false, DROP><<<grid, block, 0, st>>>(p);
+  else if (sparse) fwd16_kernel<T, D, NS, false, true, DROP><<<grid, block, 0, st>>>(p);
+  else fwd16_kernel<T, D, NS, false, false, DROP><<<grid, block, 0, st>>>(p);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch16(const FwdParams& p, bool causal, bool sparse, hipStream_t st) {
-  dim3 grid(((p.N + 127) / 128) * p.BH * (p.n_splits > 1 ? p.n_splits : 1)), block(256);
-  if (p.drop) {
-    if (causal && sparse) fwd16_kernel<T, D, true, true, true><<<grid, block, 0, st>>>(p);
-    else if (causal) fwd16_kernel<T, D, true, false, true><<<grid, block, 0, st>>>(p);
-    else if (sparse) fwd16_kernel<T, D, false, true, true><<<grid, block, 0, st>>>(p);
-    else fwd16_kernel<T, D, false, false, true><<<grid, block, 0, st>>>(p);
-  } else if (causal && sparse) fwd16_kernel<T, D, true, true, false><<<grid, block, 0, st>>>(p);
-  else if (causal) fwd16_kernel<T, D, true, false, false><<<grid, block, 0, st>>>(p);
-  else if (sparse) fwd16_kernel<T, D, false, true, false><<<grid, block, 0, st>>>(p);
-  else fwd16_kernel<T, D, false, false, false><<<grid, block, 0, st>>>(p);
-  return hipGetLastError();
+  const dim3 grid(((p.N + 127) / 128) * p.BH * (p.n_splits > 1 ? p.n_splits : 1));
+  constexpr int NS = D == 64 ? 3 : 2;
+  if (p.drop) return launch16_v<T, D, NS, true>(p, causal, sparse, grid, st);
+  if constexpr (D == 64) {
+    // Grids of at least two full rounds at four workgroups per CU run the
+    // two-slot form (four waves per SIMD, 128 VGPRs); smaller grids keep
+    // copies two tiles ahead (three slots, three waves), which shortens
+    // each workgroup.  (The dropout variant needs more than 128 VGPRs and
+    // keeps three slots.)
+    if (grid.x >= (unsigned)fwd16_large_grid()) return launch16_v<T, D, 2, false>(p, causal, sparse, grid, st);
+  }
+  return launch16_v<T, D, NS, false>(p, causal, sparse, grid, st);
 }
 
 template <int D>

@@ -10,16 +10,36 @@ namespace fa {
 enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 constexpr int MASK_TILE = 128;  // block-mask granularity (rows and columns)
 constexpr int FWD_BR = 128;     // query rows per fp32 forward workgroup (== MASK_TILE)
-// 16-bit forward: 64-key K/V tiles held in two LDS rings (K and V) of this
-// many slots each.  d = 64: 3 slots (48 KiB, three workgroups per CU, copies
-// issued two tiles ahead); d = 128: 2 slots (64 KiB, two workgroups per CU).
-constexpr int fwd16_slots(int d) { return d == 64 ? 3 : 2; }
+// Build-time alternatives of the tile and occupancy choices below, for
+// measuring them against each other (the defaults are the library's
+// choices): FA_FWD16_LARGE_GRID (workgroups from which the d = 64 forward
+// takes its two-slot form; 0 = always, a huge value = never),
+// FA_BWD_WAVES_D64 (2 or 1), FA_BWD_WAVES_D128 (1 or 2), FA_FWD8_WAVES_D64
+// (4 or 3).
+#ifndef FA_FWD16_LARGE_GRID
+#define FA_FWD16_LARGE_GRID 2048
+#endif
+#ifndef FA_BWD_WAVES_D64
+#define FA_BWD_WAVES_D64 2
+#endif
+#ifndef FA_BWD_WAVES_D128
+#define FA_BWD_WAVES_D128 1
+#endif
+#ifndef FA_FWD8_WAVES_D64
+#define FA_FWD8_WAVES_D64 4
+#endif
+// 16-bit forward: 64-key K/V tiles held in two LDS rings (K and V) of NS
+// slots each.  d = 64: NS = 3 (48 KiB, three workgroups per CU, copies issued
+// two tiles ahead) for grids below two rounds of four workgroups per CU,
+// NS = 2 (32 KiB, four workgroups per CU, copies one tile ahead) from there
+// on, without dropout; d = 128: NS = 2 (64 KiB, two workgroups per CU).
+constexpr int fwd16_large_grid() { return FA_FWD16_LARGE_GRID; }
 // Occupancy the 16-bit forward is compiled for (waves per SIMD).
-constexpr int fwd16_waves(int d) { return d == 64 ? 3 : 2; }
+constexpr int fwd16_waves(int d, int ns) { return d == 64 ? (ns == 3 ? 3 : 4) : 2; }
 // Occupancy of the unit-pipelined backward kernels (waves per SIMD): at
 // d = 128 one wave holds K, V rows and fp32 dK, dV accumulators (512
 // registers) and its workgroup takes most of the CU's LDS.
-constexpr int bwd_u_waves(int d) { return d == 64 ? 2 : 1; }
+constexpr int bwd_u_waves(int d) { return d == 64 ? FA_BWD_WAVES_D64 : FA_BWD_WAVES_D128; }
 // Decode: waves per SIMD (== workgroups per CU).  Each workgroup holds four
 // waves' two-slot rings of 32-key K and V tiles: 64 KiB at d = 64, 128 KiB at
 // d = 128.
@@ -29,7 +49,7 @@ constexpr int DEC_SPLIT_ALIGN = 128;  // key-range lengths are multiples of 4 wa
 // FP8 forward: waves per SIMD (three-slot rings of 64-key E4M3 K and V^T
 // tiles: 24 KiB at d = 64, 48 KiB at d = 128).  d = 64 fits four waves in
 // 128 VGPRs with two values spilled around (not inside) the key loop.
-constexpr int fwd8_waves(int d) { return d == 64 ? 4 : 2; }
+constexpr int fwd8_waves(int d) { return d == 64 ? FA_FWD8_WAVES_D64 : 2; }
 constexpr int FWD_MAX_MASK_TILES = 2048;  // block-mask columns the forward caches (N <= 262144)
 
 struct FwdParams {

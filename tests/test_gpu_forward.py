@@ -127,6 +127,10 @@ WIDE = [
     (2, 128, 513, 64, "f16", True),
     (1, 512, 64, 64, "bf16", True),
     (1, 600, 1, 64, "bf16", False),
+    # grids of >= 2048 workgroups at d = 64 take the two-slot ring form
+    (4, 64, 1000, 64, "bf16", False),
+    (1, 64, 4097, 64, "f16", True),
+    (3, 40, 2200, 64, "bf16", True),
 ]
 
 
@@ -142,3 +146,18 @@ def test_forward_many_heads(fa, B, H, N, d, dtype, causal):
         assert_close(f"o[{b},{h}]", f64(o[b, h]), ro, tol)
         assert_close(f"lse[{b},{h}]", f64(lse[b, h]), rl, LSE_TOL)
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+def test_forward_large_grid_block_sparse(fa):
+    """A block-sparse d = 64 grid of 2112 workgroups (two-slot ring form),
+    with a ragged tail: four heads against the oracle in full."""
+    B, H, N, d = 2, 32, 4100, 64
+    q, k, v, _ = W.draw_qkvdo(B, H, N, d, "f16", seed=4100)
+    mask = random_block_mask(N, 0.3, seed=41)
+    scale = W.scale_for(d)
+    assert B * H * (-(-N // 128)) >= 2048
+    o, lse = run_fwd(fa, q, k, v, scale, False, mask)
+    heads = [(0, 0), (1, 31), (1, 7), (0, 20)]
+    for (b, h), (ro, rl) in zip(heads, oracle_forward_heads(q, k, v, scale, False, mask, heads)):
+        assert_close(f"o[{b},{h}]", f64(o[b, h]), ro, TOL[torch.float16])
+        assert_close(f"lse[{b},{h}]", f64(lse[b, h]), rl, LSE_TOL)
