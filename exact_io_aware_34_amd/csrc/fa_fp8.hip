@@ -88,7 +88,9 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8Params p) {
   using VT = typename V8<T>::t;
   constexpr int EPT = D / 4;        // elements per lane (four lanes per row)
   __shared__ float red[4];
-  constexpr int RSB = D + 4;        // V code tile row stride in LDS (bytes)
+  // V code tile row stride in LDS (bytes): with it the dword writes below
+  // meet at most two lanes per bank and the column reads none (64 banks).
+  constexpr int RSB = D + (D == 64 ? 12 : 4);
   __shared__ __attribute__((aligned(16))) uint8_t vtile[64 * RSB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -148,8 +150,7 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8Params p) {
   float am = 0.f;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) am = fmaxf(am, fabsf(x[e]));
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+  am = wave_max(am);
   if (lane == 0) red[wave] = am;
   __syncthreads();
   am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
@@ -174,8 +175,8 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8Params p) {
       *(i32x4*)(dst + 16 * i) = i32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
     return;
   }
-  // V: transpose the block through LDS into [d][64 positions].  Rows are
-  // padded to D + 4 bytes so that the column reads below hit distinct banks.
+  // V: transpose the block through LDS into [d][64 positions] (rows padded
+  // to RSB bytes).
   // Each thread moves 4 x 4 byte blocks: the four keys of positions
   // 4j .. 4j+3 (consecutive keys) at columns 4dq .. 4dq+3, read as four
   // dwords and transposed with byte permutes into one dword per column.
@@ -246,8 +247,7 @@ __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
   // Largest value-block scale of this head.
   float mv = 0.f;
   for (int i = tid; i < nt; i += 256) mv = fmaxf(mv, svh[i]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mv = fmaxf(mv, __shfl_xor(mv, off));
+  mv = wave_max(mv);
   if (lane == 0) red_s[wave] = mv;
   __syncthreads();
   const float sv_max = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
