@@ -14,6 +14,12 @@ counted as 4*N^2*d per head for the forward and 10*N^2*d per head for the
 backward, halved for causal masking and scaled by the fraction of 128x128
 tiles the block mask keeps.  One JSON line is printed.
 
+The other workloads (long-context fp16, block-sparse d = 128, and the
+single-head N = 4096 bf16 / fp32 and N = 256 fp32 forwards) are timed the
+same way after the headline steps and reported in the `workloads` object
+(the single-head forwards through the library's default, which splits their
+key ranges over more workgroups).
+
 The decode path (fa_decode: a few queries against a long cached K/V history)
 is timed after the steps on its own workload and reported in the `decode`
 object of the same line: call time, algorithmic HBM bytes per call (16-bit K
@@ -70,7 +76,8 @@ def parse():
                     help="heads of the workload the oracle is timed on "
                          "(0: two per host core)")
     ap.add_argument("--other-workloads", default="causal_b1h12_n23400_d64_f16,"
-                    "sparse_b2h16_n16384_d128_bf16",
+                    "sparse_b2h16_n16384_d128_bf16,dense_n4096_d64_bf16,dense_n4096_d64_f32,"
+                    "dense_n256_d64_f32",
                     help="comma-separated workloads also timed (fwd + bwd) and reported "
                          "in the `workloads` object; empty for none")
     ap.add_argument("--other-steps", type=int, default=20)
@@ -196,12 +203,18 @@ def time_passes(fa, w, tensors, mask, steps, warmup, dropout_p=0.0, seed=0):
     stream = torch.cuda.current_stream()
     # With dropout the forward also writes O in fp32 for the backward's D.
     o_acc = torch.empty(q.shape, dtype=torch.float32, device=q.device) if dropout_p else None
+    # Without dropout fa.forward splits the key range of grids too small to
+    # fill the GPU (the library's choice); its workspace is allocated here.
+    ws_f = None
+    if not dropout_p and fa.forward_splits(w.B, w.H, w.N, w.d, 0) > 1:
+        ws_f = torch.empty(fa.forward_split_workspace_size(w.B, w.H, w.N, w.d, 0),
+                           dtype=torch.uint8, device=q.device)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
         fa.forward(q, k, v, causal=w.causal, scale=w.scale, block_mask=mask, out=o, lse=lse,
-                   dropout_p=dropout_p, seed=seed, o_acc=o_acc)
+                   dropout_p=dropout_p, seed=seed, o_acc=o_acc, workspace=ws_f)
         if ev is not None:
             ev[1].record(stream)
         if w.backward:
@@ -504,7 +517,8 @@ def bench_other(fa, name, steps, warmup):
     fwd_ms, bwd_ms, wall = time_passes(fa, w, tensors, mask, steps, warmup)
     out = {"B": w.B, "H": w.H, "N": w.N, "d": w.d, "dtype": w.dtype, "causal": w.causal,
            "block_sparse": w.sparse, "steps": steps, "warmup": warmup,
-           "work_fraction": round(work_fraction(w, inputs["mask"]), 5)}
+           "work_fraction": round(work_fraction(w, inputs["mask"]), 5),
+           "forward_key_runs": fa.forward_splits(w.B, w.H, w.N, w.d, 0)}
     out.update(pass_summary(w, inputs["mask"], fwd_ms, bwd_ms, wall, steps))
     if w.sparse:
         out["skip_efficiency"] = skip_efficiency(fa, w, tensors, mask, steps, fwd_ms, bwd_ms)

@@ -150,19 +150,26 @@ def forward_splits(B, H, N, d, n_splits=0) -> int:
     return int(_lib.fa_forward_splits(B, H, N, d, n_splits))
 
 
+def fa_forward_splits_used(B, H, N, d, n_splits) -> int:
+    """Key runs fa_forward_split would use (1 when the plain forward runs)."""
+    return int(_lib.fa_forward_splits(B, H, N, d, n_splits)) if n_splits != 1 else 1
+
+
 def forward_split_workspace_size(B, H, N, d, n_splits=0) -> int:
     return int(_lib.fa_forward_split_workspace_size(B, H, N, d, n_splits))
 
 
 def forward(q, k, v, causal=False, scale=None, block_mask=None, out=None, lse=None,
-            stream=None, dropout_p=0.0, seed=0, offset=0, n_splits=1, workspace=None,
+            stream=None, dropout_p=0.0, seed=0, offset=0, n_splits=0, workspace=None,
             o_acc=None):
     """Exact attention forward: returns (o, lse) with o in q's dtype, lse fp32.
     dropout_p > 0 drops probabilities with the mask fa_dropout_mask describes;
     `o_acc` (fp32, q's shape) then receives O before its rounding to q's
-    dtype, which the dropout backward needs.  n_splits != 1 runs
-    fa_forward_split (0 = the library's choice of key runs) with `workspace`
-    (allocated here when None)."""
+    dtype, which the dropout backward needs.  Without dropout the call is
+    fa_forward_split: n_splits = 0 (default) lets the library split the key
+    range of grids too small to fill the GPU (one run, i.e. fa_forward, for
+    every other grid), 1 never splits, > 1 asks for that many runs;
+    `workspace` is allocated here when None and needed."""
     _check_inputs(q, k, v)
     B, H, N, d = q.shape
     scale = default_scale(d) if scale is None else float(scale)
@@ -173,9 +180,10 @@ def forward(q, k, v, causal=False, scale=None, block_mask=None, out=None, lse=No
     _check_f32(lse, (B, H, N), "lse")
     if o_acc is not None:
         _check_f32(o_acc, (B, H, N, d), "o_acc")
-    if n_splits != 1:
-        if dropout_p or o_acc is not None:
-            raise ValueError("split key runs are not offered with dropout")
+    drop = bool(dropout_p) or o_acc is not None
+    if drop and n_splits not in (0, 1):
+        raise ValueError("split key runs are not offered with dropout")
+    if not drop and fa_forward_splits_used(B, H, N, d, n_splits) > 1:
         ws_bytes = forward_split_workspace_size(B, H, N, d, n_splits)
         if workspace is None and ws_bytes > 0:
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
@@ -183,7 +191,7 @@ def forward(q, k, v, causal=False, scale=None, block_mask=None, out=None, lse=No
         rc = _lib.fa_forward_split(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                                    scale, int(bool(causal)), _ptr(mask), DTYPE_CODES[q.dtype],
                                    int(n_splits), _ptr(workspace), nbytes, _stream(stream))
-    elif dropout_p or o_acc is not None:
+    elif drop:
         rc = _lib.fa_forward_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                                      scale, int(bool(causal)), _ptr(mask), DTYPE_CODES[q.dtype],
                                      float(dropout_p), int(seed), int(offset), _ptr(o_acc),

@@ -29,7 +29,7 @@ def run_fwd_bwd(fa, q, k, v, do, scale, causal, mask):
     dev = "cuda"
     qd, kd, vd, dod = (t.to(dev).contiguous() for t in (q, k, v, do))
     md = None if mask is None else mask.to(dev)
-    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale, block_mask=md)
+    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale, block_mask=md, n_splits=1)
     dq, dk, dv = fa.backward(qd, kd, vd, o, lse, dod, causal=causal, scale=scale, block_mask=md)
     torch.cuda.synchronize()
     return dq.cpu(), dk.cpu(), dv.cpu()
@@ -168,3 +168,29 @@ def test_backward_row_statistics(fa, B, H, N, d, dtype, causal, sparse, dropout_
     assert torch.equal(torch.isinf(lse2), torch.isinf(want))
     fin = torch.isfinite(want)
     assert (lse2[fin] - want[fin]).abs().max().item() <= 1e-6 * max(1.0, want[fin].abs().max().item())
+
+
+@pytest.mark.parametrize("N,causal", [(1000, False), (700, True), (4100, False)])
+def test_block_sparse_work_order(fa, N, causal):
+    """With a block mask the backward ranks the mask's rows (query tiles) and
+    columns (key tiles) by visible-tile count, most first, ties by index, into
+    the last region of its workspace: both must be permutations in that order
+    (every tile is computed exactly once), counted on the CPU from the mask."""
+    B, H, d = 1, 2, 64
+    q, k, v, do = W.draw_qkvdo(B, H, N, d, "bf16", seed=N + 3)
+    mask = random_block_mask(N, 0.35, seed=N + 5)
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    md = mask.cuda()
+    o, lse = fa.forward(qd, kd, vd, causal=causal, block_mask=md, n_splits=1)
+    ws = torch.zeros((fa.workspace_size(B, H, N, d),), dtype=torch.uint8, device="cuda")
+    fa.backward(qd, kd, vd, o, lse, dod, causal=causal, block_mask=md, workspace=ws)
+    torch.cuda.synchronize()
+    nt = -(-N // 128)
+    start = 2 * ((B * H * N * 4 + 255) // 256 * 256)
+    order = ws[start:start + 8 * nt].view(torch.int32).cpu().numpy()
+    m = mask.numpy().astype(bool)
+    if causal:
+        m = m & np.tril(np.ones((nt, nt), dtype=bool))
+    for got, counts in ((order[:nt], m.sum(axis=1)), (order[nt:], m.sum(axis=0))):
+        want = sorted(range(nt), key=lambda i: (-counts[i], i))
+        assert list(got) == want

@@ -65,7 +65,8 @@ def _inputs(B, H, N, d, dtype, mask_kind, scale):
 def test_edges_forward(fa, B, H, N, d, dtype, causal, mask_kind, scale):
     q, k, v, do, mask, sc = _inputs(B, H, N, d, dtype, mask_kind, scale)
     md = None if mask is None else mask.cuda()
-    o, lse = fa.forward(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=sc, block_mask=md)
+    o, lse = fa.forward(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=sc, block_mask=md,
+                        n_splits=1)
     torch.cuda.synchronize()
     o, lse = o.cpu(), lse.cpu()
     heads = [(b, h) for b in range(B) for h in range(H)]
@@ -83,7 +84,7 @@ def test_edges_backward(fa, B, H, N, d, dtype, causal, mask_kind, scale):
     q, k, v, do, mask, sc = _inputs(B, H, N, d, dtype, mask_kind, scale)
     md = None if mask is None else mask.cuda()
     qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
-    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=sc, block_mask=md)
+    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=sc, block_mask=md, n_splits=1)
     dq, dk, dv = fa.backward(qd, kd, vd, o, lse, dod, causal=causal, scale=sc, block_mask=md)
     torch.cuda.synchronize()
     dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
@@ -118,7 +119,8 @@ def test_largest_mask_grid_block_diagonal(fa, causal):
     sc = W.scale_for(d)
     mask = torch.eye(t, dtype=torch.uint8)
     qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
-    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=sc, block_mask=mask.cuda())
+    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=sc, block_mask=mask.cuda(),
+                        n_splits=1)
     dq, dk, dv = fa.backward(qd, kd, vd, o, lse, dod, causal=causal, scale=sc,
                              block_mask=mask.cuda())
     torch.cuda.synchronize()

@@ -27,7 +27,7 @@ def run_fwd(fa, q, k, v, scale, causal, mask):
     dev = "cuda"
     qd, kd, vd = (t.to(dev).contiguous() for t in (q, k, v))
     md = None if mask is None else mask.to(dev)
-    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale, block_mask=md)
+    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale, block_mask=md, n_splits=1)
     torch.cuda.synchronize()
     return o.cpu(), lse.cpu()
 

@@ -41,7 +41,7 @@ def test_graph_replays_match_eager(fa):
                       device="cuda")
 
     def step():
-        fa.forward(q, k, v, causal=True, out=o, lse=lse)
+        fa.forward(q, k, v, causal=True, out=o, lse=lse, n_splits=1)
         fa.backward(q, k, v, o, lse, do, causal=True, workspace=ws, grads=grads)
         fa.decode(xq, xk, xv, causal=True, n_splits=3, out=xo, lse=xlse, workspace=xws)
         fa.forward(q, k, v, causal=True, out=so, lse=slse, n_splits=4, workspace=sws)
@@ -61,7 +61,7 @@ def test_graph_replays_match_eager(fa):
         for dst, src in ((q, nq), (k, nk), (v, nv), (do, ndo), (xq, mq), (xk, mk), (xv, mv)):
             dst.copy_(src)
         graph.replay()
-        eo, el = fa.forward(nq, nk, nv, causal=True)
+        eo, el = fa.forward(nq, nk, nv, causal=True, n_splits=1)
         eg = fa.backward(nq, nk, nv, eo, el, ndo, causal=True)
         exo, exl = fa.decode(mq, mk, mv, causal=True, n_splits=3)
         eso, esl = fa.forward(nq, nk, nv, causal=True, n_splits=4)

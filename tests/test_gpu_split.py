@@ -74,7 +74,7 @@ def test_split_counts_agree(fa):
     scale = W.scale_for(d)
     dev = "cuda"
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
-    o1, l1 = fa.forward(qd, kd, vd, causal=True, scale=scale)
+    o1, l1 = fa.forward(qd, kd, vd, causal=True, scale=scale, n_splits=1)
     for n in (2, 3, 8, 31):
         on, ln = fa.forward(qd, kd, vd, causal=True, scale=scale, n_splits=n)
         torch.cuda.synchronize()
@@ -101,3 +101,17 @@ def test_split_rejects_dropout(fa):
     q = torch.zeros((1, 1, 256, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ValueError):
         fa.forward(q, q, q, dropout_p=0.1, n_splits=2)
+
+
+def test_default_forward_splits_small_grids(fa):
+    """fa.forward's default (n_splits = 0) is the library's choice: a single
+    head of N = 4096 (32 workgroups) runs split key ranges, bit for bit the
+    explicit n_splits = 0 call, and a full grid runs the plain forward."""
+    q, k, v, _ = W.draw_qkvdo(1, 1, 4096, 64, "bf16", seed=5)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    assert fa.forward_splits(1, 1, 4096, 64, 0) > 1
+    o0, l0 = fa.forward(qd, kd, vd)
+    o1, l1 = fa.forward(qd, kd, vd, n_splits=0)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    assert fa.forward_splits(4, 12, 8192, 64, 0) == 1

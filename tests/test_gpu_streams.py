@@ -35,7 +35,7 @@ def _inputs(B, H, N, d, dtype, seed):
 
 
 def _step(fa, q, k, v, do, causal):
-    o, lse = fa.forward(q, k, v, causal=causal)
+    o, lse = fa.forward(q, k, v, causal=causal, n_splits=1)
     dq, dk, dv = fa.backward(q, k, v, o, lse, do, causal=causal)
     return o, lse, dq, dk, dv
 
@@ -63,7 +63,7 @@ def test_concurrent_streams_match_serial(fa):
 
 def test_call_is_ordered_on_its_stream(fa):
     q, k, v, _ = _inputs(1, 2, 384, 64, "bf16", 3)
-    o_ref, lse_ref = fa.forward(q, k, v, causal=True)
+    o_ref, lse_ref = fa.forward(q, k, v, causal=True, n_splits=1)
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
     big = torch.randn(4096, 4096, device="cuda")
@@ -73,7 +73,7 @@ def test_call_is_ordered_on_its_stream(fa):
             big = big @ big * 1e-3              # keeps the stream busy before the copy
         q2 = torch.empty_like(q)
         q2.copy_(q)
-        o, lse = fa.forward(q2, k, v, causal=True)
+        o, lse = fa.forward(q2, k, v, causal=True, n_splits=1)
     torch.cuda.synchronize()
     assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref)
 
