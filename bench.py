@@ -402,7 +402,7 @@ def bench_fp8(fa, w, inputs, tensors, mask, steps, warmup, cpu_heads, with_cpu):
 
     call = timed(lambda: fa.forward_fp8(q, k, v, signs=sd, causal=w.causal, scale=w.scale,
                                         block_mask=mask, out=o, lse=lse, workspace=ws))
-    prep = timed(lambda: fa.fp8_prepare(q, k, v, sd, workspace=ws))
+    prep = timed(lambda: fa.fp8_prepare(q, k, v, sd, scale=w.scale, workspace=ws))
     mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
     f_fwd, _ = flops(w, mask.cpu() if mask is not None else None)
     tf = f_fwd / (mean(call) * 1e-3) / 1e12

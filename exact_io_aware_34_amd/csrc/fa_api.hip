@@ -155,7 +155,7 @@ int fp8_setup(fa::Fp8Params& p, const void* q, const void* k, const void* v, int
 
 extern "C" {
 
-int fa_abi_version(void) { return 3; }
+int fa_abi_version(void) { return 4; }
 
 const char* fa_status_string(int status) {
   switch (status) {
@@ -420,10 +420,10 @@ size_t fa_forward_fp8_workspace_size(int B, int H, int N, int d) {
 }
 
 int fa_fp8_prepare(const void* q, const void* k, const void* v, int B, int H, int N, int d,
-                   int dtype, const int8_t* signs, void* workspace, size_t workspace_bytes,
-                   void* stream) {
+                   float scale, int dtype, const int8_t* signs, void* workspace,
+                   size_t workspace_bytes, void* stream) {
   fa::Fp8Params p{};
-  const int rc = fp8_setup(p, q, k, v, B, H, N, d, 1.0f, dtype, signs, workspace, workspace_bytes);
+  const int rc = fp8_setup(p, q, k, v, B, H, N, d, scale, dtype, signs, workspace, workspace_bytes);
   if (rc != FA_OK) return rc;
   const hipError_t e = fa::launch_fp8(p, dtype, d, false, true, false, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;

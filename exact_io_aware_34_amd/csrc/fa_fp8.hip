@@ -6,15 +6,18 @@
 // coordinate, and then quantised per block.  The rotation here is
 // R = diag(sigma) H_d / sqrt(d) (Sylvester-Hadamard H_d, random signs sigma
 // passed in by the caller); R is orthogonal, so (Q R)(K R)^T = Q K^T.  Q and
-// K rows are rotated, V is not.  Every 64-row block of the rotated Q, of the
-// rotated K and of V gets one fp32 scale s = amax / 448 (448 is the largest
-// E4M3 value) and becomes E4M3(x * 448 / amax).  The attention itself is the
-// online-softmax forward of the 16-bit path ("Método", xyznot.com reading
-// guide) on E4M3 operands: scores S = scale * s_q s_k (Q8 K8^T) accumulate in
-// fp32 on the matrix cores, the softmax statistics stay fp32, and P is
-// rounded to E4M3 for the P V product after the value block's scale ratio
-// r_t = s_v[t] / max_t s_v[t] is folded into it, so that
-// O = max_t s_v[t] * sum_j E4M3(P_ij r_t) V8_j / l_i.
+// K rows are rotated, V is not; Q is also multiplied by c = scale * log2(e),
+// so that its products with K are scores in base-2 units.  Every 64-row
+// block of c Q R, of K R and of V gets one block scale s, the smallest power
+// of two with s * 448 >= amax (448 is the largest E4M3 value; an E8M0 scale
+// as in the OCP microscaling formats), and becomes E4M3(x / s).  The
+// attention itself is the online-softmax forward of the 16-bit path
+// ("Método", xyznot.com reading guide) on E4M3 operands: scores
+// x = s_q s_k (Q8 K8^T) accumulate in fp32 on the matrix cores, which apply
+// both power-of-two block scales exactly; the softmax statistics stay fp32;
+// P = 2^(x - m) is rounded to E4M3 for the P V product, whose matrix
+// instruction applies the value block's scale, so that
+// O = sum_j E4M3(P_ij) s_v[t(j)] V8_j / l_i.
 //
 // Two kernels:
 //   * fp8_prep_kernel: one workgroup per (Q, K or V; batch*head; 64-row
@@ -27,11 +30,14 @@
 //   * fwd8_kernel: the 16-bit forward's grid and causal / block-sparse tile
 //     skipping, 64-key K and V^T tiles in a three-slot LDS ring filled by
 //     direct global->LDS copies, S^T = K Q^T and O^T += V^T P^T on
-//     v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, neutral block scales,
-//     fp32 accumulation).  Lane l holds query l % 32 at 16 keys of each
-//     32-key unit, which are exactly its 32 contraction slots of the P V
-//     product over the tile's 64 keys: P goes from the score accumulators to
-//     the operand with no shuffle.
+//     v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, the block scales as the
+//     instruction's E8M0 scale operands, fp32 accumulation).  The score
+//     accumulators start at -m (the running reference), so the matrix core
+//     also subtracts it and the exponentials take the accumulators as they
+//     are.  Lane l holds query l % 32 at 16 keys of each 32-key unit, which
+//     are exactly its 32 contraction slots of the P V product over the
+//     tile's 64 keys: P goes from the score accumulators to the operand with
+//     no shuffle.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -46,10 +52,28 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kE4M3Max = 448.f;
 
-__device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c) {
-  // Formats 0/0: both operands E4M3; scale operands 127 = 2^0 (E8M0).
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+// c + (2^(ea-127) A)(2^(eb-127) B): formats 0/0, both operands E4M3; ea and eb
+// are E8M0 exponents (byte 0 of the scale operands), the same for every lane.
+__device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c, int ea, int eb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
 }
+
+// The smallest power of two s >= amax / 448 (so that |x| / s <= 448 for the
+// block), at least 2^-126; 1 for an all-zero block.  With amax = f 2^E,
+// f in [0.5, 1), and 448 = 0.875 * 2^9: 448 * 2^k >= amax holds from
+// k = E - 9 when f <= 0.875 and from k = E - 8 otherwise; f <= 0.875 is the
+// stored mantissa of amax <= 0.75 * 2^23.
+__device__ __forceinline__ float pow2_block_scale(float amax) {
+  if (!(amax > 0.f)) return 1.f;
+  const uint32_t b = __float_as_uint(amax);
+  const int eb = (int)(b >> 23);           // biased exponent: E = eb - 126
+  int k = eb - 135 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  if (eb == 0 || k < -126) k = -126;       // subnormal or tiny amax
+  return __uint_as_float((uint32_t)(k + 127) << 23);
+}
+
+// E8M0 exponent of a power-of-two scale (its biased fp32 exponent).
+__device__ __forceinline__ int e8m0_of(float s) { return (int)(__float_as_uint(s) >> 23); }
 
 // Four fp32 values to four E4M3 bytes (a in the lowest byte).  The
 // conversion rounds to nearest even; it does not saturate, so every caller
@@ -141,9 +165,12 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8Params p) {
       const float y = quad_xor2(x[e]);
       x[e] = (qd & 2) ? y - x[e] : x[e] + y;
     }
-    const float rs = p.rsqrt_d;
+    const float rs = z == 0 ? p.rsqrt_d * p.scale_log2e : p.rsqrt_d;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) x[e] *= rs;
+  } else if (z == 0) {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) x[e] *= p.scale_log2e;
   }
 
   // Block amax over the 64 rows.
@@ -154,10 +181,11 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8Params p) {
   if (lane == 0) red[wave] = am;
   __syncthreads();
   am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float inv = am > 0.f ? kE4M3Max / am : 1.f;
+  const float bs = pow2_block_scale(am);
+  const float inv = __uint_as_float((uint32_t)(254 - e8m0_of(bs)) << 23);   // 1 / bs, exact
   if (tid == 0) {
     float* sc = z == 0 ? p.sq : (z == 1 ? p.sk : p.sv);
-    sc[(size_t)bh * nt + t] = am > 0.f ? am / kE4M3Max : 1.f;
+    sc[(size_t)bh * nt + t] = bs;
   }
 
   int w[EPT / 4];
@@ -220,7 +248,6 @@ __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
   // (lanes 2.. of the copy repeat them).
   __shared__ __attribute__((aligned(16))) float sc_s[NS][64];
   __shared__ uint8_t mask_s[SPARSE ? FWD_MAX_MASK_TILES : 1];
-  __shared__ float red_s[4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -242,16 +269,10 @@ __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
   const float* __restrict__ svh = p.sv + (size_t)bh * nt;
   const int q0w = qt * BR + wave * 32;
 
-  if (SPARSE)
+  if (SPARSE) {
     for (int i = tid; i < p.mask_tiles; i += 256) mask_s[i] = p.mask[(size_t)qt * p.mask_tiles + i];
-  // Largest value-block scale of this head.
-  float mv = 0.f;
-  for (int i = tid; i < nt; i += 256) mv = fmaxf(mv, svh[i]);
-  mv = wave_max(mv);
-  if (lane == 0) red_s[wave] = mv;
-  __syncthreads();
-  const float sv_max = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
-  const float lsv_max = __log2f(sv_max);
+    __syncthreads();
+  }
 
   // Per-lane LDS byte offsets.  K (A operand of S^T): key 32 u + l32, bytes
   // 64 h + 32 g .. + 31.  V^T (A operand of O^T): row 32 db + l32, bytes
@@ -327,15 +348,21 @@ __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
       qf[h] = q < N ? *(const i32x8*)(p.q8 + ((size_t)bh * p.Npad + q) * D + 64 * h + 32 * g)
                     : i32x8{};
   }
-  const float sq_w = p.sq[(size_t)bh * nt + min(q0w, N - 1) / 64];
+  const int eq = e8m0_of(p.sq[(size_t)bh * nt + min(q0w, N - 1) / 64]);
   wait_all_loads();
 
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-  float m_run = -1e30f;   // running reference, log2 units of the scaled score
-  float l_run = 0.f;      // this lane's share of sum exp2(x - m_run)
-  const float c0 = p.scale_log2e * sq_w;
+  // Running reference m (base-2 score units) and this lane's share of
+  // sum 2^(x - m).  The score accumulators start at -m (negm), so each MFMA
+  // chain ends holding x - m.  No reference exists until a query's first
+  // visible key: while its sum is 0 every tile takes the reference step.
+  float m_run = 0.f, l_run = 0.f;
+  f32x16 negm = f32x16{};
+  // Opaque to the compiler, so that it keeps the 16 registers instead of
+  // rebuilding the splat before every tile.
+  asm volatile("" : "+v"(negm));
 
   int slot = 0;
   while (jq[0] < kt_end) {
@@ -347,16 +374,17 @@ __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
     if (j * BC <= last_key) {
       const uint8_t* kt = kvs + slot * TB;
       const uint8_t* vt = kvs + slot * TB;   // V^T offsets already include NS * TB
+      const float2 sc = *(const float2*)&sc_s[slot][0];
+      const int ek = e8m0_of(sc.x), ev = e8m0_of(sc.y);
       f32x16 s[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        s[u] = f32x16{};
 #pragma unroll
         for (int h = 0; h < DH; ++h) {
           const i32x4 lo = *(const i32x4*)(kt + koff[u][h][0]);
           const i32x4 hi = *(const i32x4*)(kt + koff[u][h][1]);
           const i32x8 kf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          s[u] = mfma_f8(kf, qf[h], s[u]);
+          s[u] = mfma_f8(kf, qf[h], h == 0 ? negm : s[u], ek, eq);
         }
       }
       // Scores past this lane's last visible key become -inf.
@@ -370,14 +398,9 @@ __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
             if (8 * (r >> 2) + (r & 3) > lim) s[u][r] = -INFINITY;
         }
       }
-      const float2 sc = *(const float2*)&sc_s[slot][0];
-      const float cj = c0 * sc.x;                         // raw accumulator -> log2 units
-      const float lr = __log2f(sc.y) - lsv_max;           // log2 r_t <= 0
-      const float inv_r = fast_exp2(-lr);                 // 1 / r_t
       i32x8 pk;
-      // p' = exp2(x - m_run) * r_t, packed to E4M3; returns the lane's sum of p'.
+      // P = 2^(x - m), packed to E4M3; returns the lane's sum of P.
       auto exps = [&]() {
-        const float off = lr - m_run;
         float ls0, ls1;  // start at the first terms, not at 0
 #pragma unroll
         for (int u = 0; u < 2; ++u)
@@ -385,7 +408,7 @@ __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
           for (int w4 = 0; w4 < 4; ++w4) {
             float e[4];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) e[b] = fast_exp2(fmaf(s[u][4 * w4 + b], cj, off));
+            for (int b = 0; b < 4; ++b) e[b] = fast_exp2(s[u][4 * w4 + b]);
             const bool first = u == 0 && w4 == 0;
             ls0 = first ? e[0] + e[1] : ls0 + (e[0] + e[1]);
             ls1 = first ? e[2] + e[3] : ls1 + (e[2] + e[3]);
@@ -395,27 +418,40 @@ __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
       };
       float ls = exps();
       // The reference moves only when some lane's tile sum exceeds 2^8 (so
-      // every packed value stays below 448); O, l and lse share it.
-      if (wave_any(!(ls <= 256.f))) {
+      // every packed value stays below 448) or some query has no reference
+      // yet; O, l and lse share it.  Both lanes of a query (l, l ^ 32) take
+      // the same step: max over the query's scores of the tile, x - m.
+      if (wave_any(!(ls <= 256.f) || l_run == 0.f)) {
         float mx = s[0][0];
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[u][r]);
-        const float m_new = fmaxf(m_run, half_swap_max(mx * cj));
-        const float alpha = fast_exp2(m_run - m_new);
-        m_run = m_new;
+        mx = half_swap_max(mx);
+        // A query with earlier terms only moves up; a fresh one moves to its
+        // tile max (if it has a visible key here), and its O and l are 0.
+        const bool fresh = half_swap_sum(l_run) == 0.f;
+        const float step = fresh ? (mx > -INFINITY ? mx : 0.f) : fmaxf(mx, 0.f);
+        const float alpha = fresh ? 0.f : fast_exp2(-step);
+        m_run += step;
         l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[db] *= alpha;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) negm[r] = -m_run;
+        asm volatile("" : "+v"(negm));
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[u][r] -= step;
         ls = exps();
       }
-      l_run = fmaf(ls, inv_r, l_run);
+      l_run += ls;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const i32x4 lo = *(const i32x4*)(vt + voff[db][0]);
         const i32x4 hi = *(const i32x4*)(vt + voff[db][1]);
-        o[db] = mfma_f8(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pk, o[db]);
+        o[db] = mfma_f8(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pk, o[db], ev, 127);
       }
     }
     jq[0] = jq[1];
@@ -424,9 +460,9 @@ __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
     slot = slot == NS - 1 ? 0 : slot + 1;
   }
 
-  // Epilogue: O = sv_max * O / l, lse = (m + log2 l) * ln 2.
+  // Epilogue: O = O / l, lse = (m + log2 l) * ln 2.
   const float lt = half_swap_sum(l_run);
-  const float inv = lt > 0.f ? sv_max / lt : 0.f;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const int q = q0w + l32;
   if (q < N) {
     T* orow = (T*)p.o + ((size_t)bh * N + q) * D;

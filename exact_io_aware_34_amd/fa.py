@@ -42,7 +42,8 @@ _lib.fa_decode_workspace_size.restype = ctypes.c_size_t
 _lib.fa_forward_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _i, _vp, _vp,
                                 ctypes.c_size_t, _vp]
 _lib.fa_forward_fp8.restype = _i
-_lib.fa_fp8_prepare.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.fa_fp8_prepare.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp, ctypes.c_size_t,
+                                _vp]
 _lib.fa_fp8_prepare.restype = _i
 _lib.fa_forward_fp8_workspace_size.argtypes = [_i, _i, _i, _i]
 _lib.fa_forward_fp8_workspace_size.restype = ctypes.c_size_t
@@ -342,11 +343,13 @@ def _fp8_args(q, k, v, signs, workspace):
     return workspace
 
 
-def fp8_prepare(q, k, v, signs=None, workspace=None, stream=None):
-    """Rotation + block quantisation only; returns the filled workspace."""
+def fp8_prepare(q, k, v, signs=None, scale=None, workspace=None, stream=None):
+    """Rotation + block quantisation only, for softmax scale `scale` (default
+    1/sqrt(d)); returns the filled workspace."""
     workspace = _fp8_args(q, k, v, signs, workspace)
     B, H, N, d = q.shape
-    rc = _lib.fa_fp8_prepare(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, DTYPE_CODES[q.dtype],
+    scale = default_scale(d) if scale is None else float(scale)
+    rc = _lib.fa_fp8_prepare(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, scale, DTYPE_CODES[q.dtype],
                              _ptr(signs), _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _stream(stream))
     if rc != 0:

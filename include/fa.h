@@ -264,16 +264,18 @@ int fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, floa
  * 3).  Here:
  *   rotation      R = diag(signs) H_d / sqrt(d), H_d the Sylvester-Hadamard
  *                 matrix; Q and K rows are multiplied by R (Q K^T is
- *                 unchanged), V is not;
- *   quantisation  every 64-row block of R-rotated Q, of R-rotated K and of V:
- *                 scale s = amax / 448 (1 for an all-zero block), codes
- *                 E4M3(x * 448 / amax) (OCP E4M3, round to nearest even);
- *   attention     S = scale * s_q s_k (Q8 K8^T) with fp32 accumulation on the
- *                 FP8 matrix cores, fp32 online softmax (running max m, sum l),
- *                 P rounded to E4M3 after the value block's scale ratio
- *                 r_t = s_v[t] / max_t s_v[t] is folded into it,
- *                 O = max_t s_v[t] * sum_j E4M3(P_ij r_t) V8_j / l_i,
- *                 lse = m + ln l.
+ *                 unchanged), V is not; Q is also multiplied by
+ *                 c = scale * log2(e), so Q K^T comes out in base-2 units;
+ *   quantisation  every 64-row block of c Q R, of K R and of V: scale s, the
+ *                 smallest power of two with 448 s >= amax (at least 2^-126;
+ *                 1 for an all-zero block: an E8M0 block scale), codes
+ *                 E4M3(x / s) (OCP E4M3, round to nearest even);
+ *   attention     x = s_q s_k (Q8 K8^T) with fp32 accumulation on the FP8
+ *                 matrix cores (the block scales applied exactly by the
+ *                 instruction), fp32 online softmax in base 2 (running
+ *                 reference m, sum l of 2^(x - m)), P = 2^(x - m) rounded to
+ *                 E4M3, O = sum_j E4M3(P_ij) s_v[t(j)] V8_j / l_i,
+ *                 lse = (m + log2 l) ln 2.
  * The result approximates exact attention to FP8 precision (a few percent
  * of |O| on N(0, 1) inputs); it is not exact.
  *
@@ -299,10 +301,12 @@ int fa_forward_fp8(const void* q, const void* k, const void* v, void* o, float* 
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* The rotation and quantisation step of fa_forward_fp8 alone: fills the
- * workspace regions Q8, K8, V8T, s_q, s_k, s_v described above. */
+ * workspace regions Q8, K8, V8T, s_q, s_k, s_v described above.  `scale` is
+ * the softmax scale the codes are prepared for (Q's codes hold scale * log2(e)
+ * times Q R); it must be finite and > 0. */
 int fa_fp8_prepare(const void* q, const void* k, const void* v, int B, int H, int N, int d,
-                   int dtype, const int8_t* signs, void* workspace, size_t workspace_bytes,
-                   void* stream);
+                   float scale, int dtype, const int8_t* signs, void* workspace,
+                   size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace fa_forward_fp8 and fa_fp8_prepare need (0 on bad input). */
 size_t fa_forward_fp8_workspace_size(int B, int H, int N, int d);
@@ -310,8 +314,9 @@ size_t fa_forward_fp8_workspace_size(int B, int H, int N, int d);
 /* Static, human-readable text for a status code. */
 const char* fa_status_string(int status);
 
-/* Library ABI version (this header: 3; 2 added fa_forward_split*, 3 the fp32
- * output o_acc of the dropout calls). */
+/* Library ABI version (this header: 4; 2 added fa_forward_split*, 3 the fp32
+ * output o_acc of the dropout calls, 4 power-of-two FP8 block scales and the
+ * scale argument of fa_fp8_prepare). */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

@@ -68,6 +68,7 @@ from .fp8 import (  # noqa: F401
     fp8_forward,
     fp8_forward_head,
     hadamard,
+    pow2_scale,
     rotate,
 )
 from .online import (  # noqa: F401

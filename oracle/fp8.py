@@ -14,19 +14,23 @@ in its order:
    matrix (entries +-1, H_d H_d^T = d I) and sigma a vector of random signs
    (drawn by the caller and passed in).  R is orthogonal, so
    (q R)(k R)^T = q k^T: the scores are unchanged in exact arithmetic.
-   Q and K rows are rotated; V is not (its rotation would not cancel).
-2. Per-block quantisation.  Each block of `block` consecutive rows of the
-   rotated Q, the rotated K and of V gets one scale s = amax / 448 (448 is
-   the largest finite E4M3 value; s = 1 for an all-zero block) and its
-   entries become e4m3(x * 448 / amax).
-3. Scores from the quantised operands, s_ij = scale * s_q s_k <q8_i, k8_j>
-   (exact: every FP8 product is exact in float64), softmax statistics m, l
-   and lse = m + ln l in float64.
-4. Probabilities in FP8 for the P V product: P_ij = exp(s_ij - m_i) times
-   r_t = s_v[t] / max_t s_v[t] for the value block t of key j, rounded to
-   E4M3 (folding the value block's scale into P keeps one scale per head for
-   the product); o_i = max_t s_v[t] * sum_j e4m3(P_ij r_t) v8_j / l_i, with
-   l_i the sum of the unrounded P_ij.
+   Q and K rows are rotated; V is not (its rotation would not cancel).  The
+   rotated Q is also multiplied by c = scale * log2(e), so that the scores
+   below come out in base-2 units (the page leaves open where the softmax
+   scale enters; here it is quantised with Q).
+2. Per-block quantisation.  Each block of `block` consecutive rows of c Q R,
+   of K R and of V gets one scale s, the smallest power of two with
+   448 s >= amax (448 is the largest finite E4M3 value; s = 1 for an
+   all-zero block, and s >= 2^-126): a shared power-of-two scale as in the
+   OCP microscaling formats.  Its entries become e4m3(x / s); |x / s| <= 448.
+3. Scores from the quantised operands in base 2, x_ij = s_q s_k <q8_i, k8_j>
+   (exact: every FP8 product is exact in float64, and so are the
+   power-of-two scales), softmax statistics m = max_j x_ij,
+   l = sum_j 2^(x_ij - m) and lse = (m + log2 l) ln 2 in float64.
+4. Probabilities in FP8 for the P V product: P_ij = 2^(x_ij - m_i), rounded
+   to E4M3, each multiplied by its value block's scale s_v[t(j)]:
+   o_i = sum_j e4m3(P_ij) s_v[t(j)] v8_j / l_i, with l_i the sum of the
+   unrounded P_ij.
 
 E4M3 is the OCP 8-bit format: 1 sign, 4 exponent (bias 7) and 3 mantissa
 bits, no infinities, largest finite value 448, smallest normal 2^-6,
@@ -73,8 +77,22 @@ def rotate(x, signs):
     return (x * np.asarray(signs, dtype=np.float64)) @ hadamard(d) / math.sqrt(d)
 
 
+def pow2_scale(amax):
+    """The smallest power of two s with 448 s >= amax, at least 2^-126; 1 for
+    amax = 0.  The comparisons 448 * 2^k >= amax are exact in float64."""
+    amax = float(amax)
+    if amax == 0.0:
+        return 1.0
+    k = math.ceil(math.log2(amax / E4M3_MAX))
+    while E4M3_MAX * 2.0 ** k < amax:
+        k += 1
+    while E4M3_MAX * 2.0 ** (k - 1) >= amax:
+        k -= 1
+    return 2.0 ** max(k, -126)
+
+
 def block_quantize(x, block, quantize=e4m3):
-    """Per-block E4M3 quantisation of the rows of x.
+    """Per-block E4M3 quantisation of the rows of x with power-of-two scales.
 
     Returns (x8, scales): x8 holds the E4M3 values (as float64), scales one
     float64 per block of `block` rows, so that x ~= x8 * scale of its block.
@@ -88,8 +106,8 @@ def block_quantize(x, block, quantize=e4m3):
         rows = slice(b * block, min(n, (b + 1) * block))
         amax = float(np.max(np.abs(x[rows]))) if x[rows].size else 0.0
         if amax > 0:
-            scales[b] = amax / E4M3_MAX
-            x8[rows] = quantize(x[rows] * (E4M3_MAX / amax))
+            scales[b] = pow2_scale(amax)
+            x8[rows] = quantize(x[rows] / scales[b])
     return x8, scales
 
 
@@ -102,41 +120,41 @@ def fp8_forward_head(q, k, v, scale, causal=False, block_mask=None, signs=None, 
     turns the method into exact attention (a pin of the composition).
     `rows` restricts the output to those query rows (the operands are still
     quantised whole).  terms=True also returns the step-4 quantities as a
-    dict: p (the unrounded P_ij = exp(s_ij - m_i), 0 off the visible keys),
-    r (per key), v8, sv_max and l, with o = sv_max (e4m3(p r) @ v8) / l, and
-    s_abs = scale s_q s_k <|q8_i|, |k8_j|> (the scores' sum of absolute
-    products).
+    dict: p (the unrounded P_ij = 2^(x_ij - m_i), 0 off the visible keys),
+    sv (the value-block scale of each key), v8 and l, with
+    o = (e4m3(p) * sv) @ v8 / l, and s_abs = s_q s_k <|q8_i|, |k8_j|> (the
+    base-2 scores' sum of absolute products).
     """
     q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
     n, d = q.shape
     if signs is not None:
         q, k = rotate(q, signs), rotate(k, signs)
+    c = scale * math.log2(math.e)
 
-    q8, sq = block_quantize(q, block, quantize)
+    q8, sq = block_quantize(q * c, block, quantize)
     k8, sk = block_quantize(k, block, quantize)
     v8, sv = block_quantize(v, block, quantize)
     rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
     rq = np.repeat(sq, block)[:n][rows]
     rk = np.repeat(sk, block)[:n]
-    s = scale * (q8[rows] * rq[:, None]) @ (k8 * rk[:, None]).T
+    x = (q8[rows] * rq[:, None]) @ (k8 * rk[:, None]).T      # base-2 scores
     ok = allowed(rows, n, causal, block_mask)
-    s = np.where(ok, s, -np.inf)
-    m = s.max(axis=1)
+    x = np.where(ok, x, -np.inf)
+    m = x.max(axis=1)
     empty = ~np.isfinite(m)
     m_safe = np.where(empty, 0.0, m)
-    p = np.exp(s - m_safe[:, None])                   # 0 where not allowed
+    p = np.exp2(x - m_safe[:, None])                  # 0 where not allowed
     ell = p.sum(axis=1)
-    sv_max = float(sv.max())
-    r = np.repeat(sv / sv_max, block)[:n]
-    p8 = quantize(p * r[None, :])
+    svk = np.repeat(sv, block)[:n]
+    p8 = quantize(p)
     with np.errstate(invalid="ignore", divide="ignore"):
-        o = sv_max * (p8 @ v8) / ell[:, None]
-        lse = m_safe + np.log(ell)
+        o = (p8 * svk[None, :]) @ v8 / ell[:, None]
+        lse = (m_safe + np.log2(ell)) * math.log(2.0)
     o[empty] = 0.0
     lse[empty] = -np.inf
     if terms:
-        s_abs = scale * (np.abs(q8[rows]) * rq[:, None]) @ (np.abs(k8) * rk[:, None]).T
-        return o, lse, {"p": p, "r": r, "v8": v8, "sv_max": sv_max, "l": ell, "s_abs": s_abs}
+        s_abs = (np.abs(q8[rows]) * rq[:, None]) @ (np.abs(k8) * rk[:, None]).T
+        return o, lse, {"p": p, "sv": svk, "v8": v8, "l": ell, "s_abs": s_abs}
     return o, lse
 
 

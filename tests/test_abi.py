@@ -33,7 +33,7 @@ def lib():
     L.fa_decode_workspace_size.restype = ctypes.c_size_t
     L.fa_forward_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, vp,
                                  ctypes.c_size_t, vp]
-    L.fa_fp8_prepare.argtypes = [vp, vp, vp, i, i, i, i, i, vp, vp, ctypes.c_size_t, vp]
+    L.fa_fp8_prepare.argtypes = [vp, vp, vp, i, i, i, i, f, i, vp, vp, ctypes.c_size_t, vp]
     L.fa_forward_fp8_workspace_size.argtypes = [i, i, i, i]
     L.fa_forward_fp8_workspace_size.restype = ctypes.c_size_t
     u64, u32 = ctypes.c_uint64, ctypes.c_uint32
@@ -68,7 +68,7 @@ def test_header_declares_the_boundary():
 def test_every_declared_symbol_is_exported(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.fa_abi_version() == 3
+    assert lib.fa_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -230,8 +230,13 @@ def test_fp8_validation(lib):
     assert f8(lib, ws=ctypes.c_void_p((1 << 20) + 16)) == -3   # not 256-byte aligned
     need = lib.fa_forward_fp8_workspace_size(2, 3, 100, 64)
     assert f8(lib, ws_bytes=need - 1) == -3
-    assert lib.fa_fp8_prepare(FAKE, FAKE, FAKE, 2, 3, 100, 64, 2, None, None, 0, None) == -3
-    assert lib.fa_fp8_prepare(None, FAKE, FAKE, 2, 3, 100, 64, 2, None, FAKE, need, None) == -1
+    assert lib.fa_fp8_prepare(FAKE, FAKE, FAKE, 2, 3, 100, 64, 0.125, 2, None, None, 0, None) == -3
+    assert lib.fa_fp8_prepare(None, FAKE, FAKE, 2, 3, 100, 64, 0.125, 2, None, FAKE, need,
+                              None) == -1
+    assert lib.fa_fp8_prepare(FAKE, FAKE, FAKE, 2, 3, 100, 64, 0.0, 2, None, FAKE, need,
+                              None) == -1                      # scale must be finite and > 0
+    assert lib.fa_fp8_prepare(FAKE, FAKE, FAKE, 2, 3, 100, 64, float("nan"), 2, None, FAKE, need,
+                              None) == -1
 
 
 def test_dropout_validation(lib):

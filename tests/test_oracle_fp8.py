@@ -6,13 +6,17 @@
   the count of distinct outputs.
 * hadamard against scipy.linalg.hadamard; H H^T = d I.
 * rotate: the d = 2 closed form, norms and dot products preserved.
-* block_quantize: each block's largest magnitude maps to exactly 448, the
-  relative error of every normal-range entry is at most 2^-4, zero blocks.
+* pow2_scale: closed forms at and around 448 * 2^k, and brute force over k
+  (the smallest power of two whose 448 multiple reaches amax).
+* block_quantize: every scale is that power of two, each block's largest
+  magnitude maps into (224, 448], the relative error of every normal-range
+  entry is at most 2^-4, zero blocks.
 * fp8_forward_head: with the identity in place of e4m3 it is exact attention
   (with or without the rotation, causal, masked) -- the rotation cancels and
-  every scale folds back; with e4m3 its error against exact attention is that
+  every scale, the base-2 factor included, folds back; with e4m3 its error
+  against exact attention is that
   of 3-bit mantissas; with outliers in Q and K the rotation lowers the error
-  on every seed, by about 2x on lse on average (the marketmaker.cc page
+  on every seed, by about 2.3x on lse on average (the marketmaker.cc page
   reports 2.6x for the method on its own inputs).
 * Planted slips in copies of the functions fail these pins.
 """
@@ -79,6 +83,18 @@ def test_rotate():
     assert not np.allclose(rx, x)
 
 
+def test_pow2_scale():
+    assert F.pow2_scale(0.0) == 1.0
+    assert F.pow2_scale(448.0) == 1.0 and F.pow2_scale(448.0 * (1 + 2 ** -40)) == 2.0
+    assert F.pow2_scale(224.0) == 0.5 and F.pow2_scale(224.0 * (1 + 2 ** -40)) == 1.0
+    assert F.pow2_scale(1.0) == 2.0 ** -8 and F.pow2_scale(1.75) == 2.0 ** -8
+    assert F.pow2_scale(1.76) == 2.0 ** -7
+    assert F.pow2_scale(1e-300) == 2.0 ** -126                 # clamped
+    for a in np.concatenate([2.0 ** RNG.uniform(-100, 100, 2000), 448.0 * 2.0 ** np.arange(-20, 21)]):
+        k = next(k for k in range(-200, 200) if 448.0 * 2.0 ** k >= a)    # brute force
+        assert F.pow2_scale(a) == 2.0 ** max(k, -126), a
+
+
 def test_block_quantize():
     x = RNG.standard_normal((150, 64)) * np.repeat([1.0, 30.0, 0.01], 50)[:, None]
     x[100:150] = 0.0
@@ -86,7 +102,9 @@ def test_block_quantize():
     assert sc.shape == (3,) and sc[2] == 1.0 and np.all(x8[128:] == 0)
     for b in range(2):
         blk = x8[64 * b: 64 * (b + 1)]
-        assert np.max(np.abs(blk)) == 448.0
+        amax = np.abs(x[64 * b: 64 * (b + 1)]).max()
+        assert sc[b] == F.pow2_scale(amax) and sc[b] >= amax / 448 > sc[b] / 2
+        assert 224.0 < np.max(np.abs(blk)) <= 448.0
     deq = x8 * np.repeat(sc, 64)[:150, None]
     normal = np.abs(x8) >= 2 ** -6
     rel = np.abs(deq - x)[normal] / np.abs(x)[normal]
@@ -142,8 +160,9 @@ def outlier_qkv(n, d, rng, frac=1e-3, sd=10.0):
 
 
 def test_rotation_reduces_error_with_outliers():
-    # Ten seeds of this recipe gave lse-error ratios 1.38..3.61 (mean 1.97)
-    # and O-error ratios 1.07..1.36 (mean 1.22); six are checked here.
+    # Ten seeds of this recipe gave lse-error ratios 1.87..6.42 (mean 3.14)
+    # and O-error ratios 1.30..1.72 (mean 1.44); the first six (lse mean
+    # 2.33, O mean 1.41) are checked here.
     ratios_lse, ratios_o = [], []
     for seed in range(6):
         rng = np.random.default_rng(100 + seed)
@@ -154,27 +173,31 @@ def test_rotation_reduces_error_with_outliers():
         orr, lr = F.fp8_forward_head(q, k, v, 0.125, True, None, s)
         ratios_lse.append(_rms(ln - rl) / _rms(lr - rl))
         ratios_o.append(_rms(on - ro) / _rms(orr - ro))
-    assert min(ratios_lse) > 1.2 and np.mean(ratios_lse) > 1.6, ratios_lse
-    assert min(ratios_o) > 1.0 and np.mean(ratios_o) > 1.1, ratios_o
+    assert min(ratios_lse) > 1.5 and np.mean(ratios_lse) > 2.0, ratios_lse
+    assert min(ratios_o) > 1.15 and np.mean(ratios_o) > 1.25, ratios_o
 
 
 def test_terms_recompose_the_output():
     """The step-4 quantities returned with terms=True give back o and lse:
-    o = sv_max (e4m3(p r) @ v8) / l, lse = max_j s_ij + ln l (exp(s - m)
+    o = (e4m3(p) sv) @ v8 / l, lse = (max_j x_ij + log2 l) ln 2 (2^(x - m)
     sums to l, and p is 1 at each row's max)."""
     n, d = 150, 64
     q, k, v = (RNG.standard_normal((n, d)) for _ in range(3))
+    v[64:128] *= 20.0                                            # a value block of its own scale
     s = RNG.choice([-1.0, 1.0], d)
     o, l, t = F.fp8_forward_head(q, k, v, 0.125, True, None, s, terms=True)
-    o2 = t["sv_max"] * (F.e4m3(t["p"] * t["r"][None, :]) @ t["v8"]) / t["l"][:, None]
-    np.testing.assert_allclose(o2, o, rtol=0, atol=1e-14)
+    o2 = (F.e4m3(t["p"]) * t["sv"][None, :]) @ t["v8"] / t["l"][:, None]
+    np.testing.assert_allclose(o2, o, rtol=0, atol=1e-13)
     assert np.allclose(t["p"].max(axis=1), 1.0) and np.allclose(t["p"].sum(axis=1), t["l"])
     assert np.all(np.triu(t["p"], 1) == 0)                      # causal: nothing above
-    assert t["r"].max() == 1.0 and np.all(t["r"] > 0)
-    # s_abs bounds |s| and equals it where every product has one sign
+    _, sv = F.block_quantize(v, 64)
+    np.testing.assert_array_equal(t["sv"], np.repeat(sv, 64)[:n])
+    assert sv[1] >= 8 * max(sv[0], sv[2])
+    # s_abs bounds |x| and equals it where every product has one sign
     o3, l3, t3 = F.fp8_forward_head(np.abs(q), np.abs(k), v, 0.125, False, None, None,
                                     terms=True)
-    np.testing.assert_allclose(t3["s_abs"].max(axis=1) + np.log(t3["l"]), l3, atol=1e-12)
+    np.testing.assert_allclose((t3["s_abs"].max(axis=1) + np.log2(t3["l"])) * math.log(2), l3,
+                               atol=1e-12)
 
 
 def test_rows_selects_query_rows():
@@ -202,16 +225,28 @@ def _forward_q_only_rotated(q, k, v, scale, causal, signs):
     return F.fp8_forward_head(F.rotate(q, signs), k, v, scale, causal, None, None, quantize=_ident)
 
 
-def _forward_without_v_fold(q, k, v, scale, causal):
+def _forward_one_v_scale(q, k, v, scale, causal):
+    """Slip: every value block multiplied by the largest value-block scale."""
     q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
     n = q.shape[0]
-    q8, sq = F.block_quantize(q, 64, _ident)
+    c = scale * math.log2(math.e)
+    q8, sq = F.block_quantize(q * c, 64, _ident)
     k8, sk = F.block_quantize(k, 64, _ident)
     v8, sv = F.block_quantize(v, 64, _ident)
-    s = scale * (q8 * np.repeat(sq, 64)[:n, None]) @ (k8 * np.repeat(sk, 64)[:n, None]).T
-    s = np.where(oracle.allowed(np.arange(n), n, causal), s, -np.inf)
-    p = np.exp(s - s.max(axis=1, keepdims=True))
+    x = (q8 * np.repeat(sq, 64)[:n, None]) @ (k8 * np.repeat(sk, 64)[:n, None]).T
+    x = np.where(oracle.allowed(np.arange(n), n, causal), x, -np.inf)
+    p = np.exp2(x - x.max(axis=1, keepdims=True))
     return sv.max() * (p @ v8) / p.sum(axis=1, keepdims=True)
+
+
+def _forward_natural_exp(q, k, v, scale, causal):
+    """Slip: base-2 scores fed to a natural exponential."""
+    q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    n = q.shape[0]
+    x = (q * scale * math.log2(math.e)) @ k.T
+    x = np.where(oracle.allowed(np.arange(n), n, causal), x, -np.inf)
+    p = np.exp(x - x.max(axis=1, keepdims=True))
+    return (p @ v) / p.sum(axis=1, keepdims=True)
 
 
 def test_pins_catch_planted_slips():
@@ -227,5 +262,7 @@ def test_pins_catch_planted_slips():
     ro, _ = oracle.forward_head(q, k, v, 0.125, True)
     wo, _ = _forward_q_only_rotated(q, k, v, 0.125, True, s)
     assert np.abs(wo - ro).max() > 1e-3
-    wo = _forward_without_v_fold(q, k, v, 0.125, True)
+    wo = _forward_one_v_scale(q, k, v, 0.125, True)
+    assert np.abs(wo - ro).max() > 1e-3
+    wo = _forward_natural_exp(q, k, v, 0.125, True)
     assert np.abs(wo - ro).max() > 1e-3
