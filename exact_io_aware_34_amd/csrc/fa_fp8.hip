@@ -413,6 +413,10 @@ __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
             ls0 = first ? e[0] + e[1] : ls0 + (e[0] + e[1]);
             ls1 = first ? e[2] + e[3] : ls1 + (e[2] + e[3]);
             pk[4 * u + w4] = pack_e4m3(e[0], e[1], e[2], e[3]);
+            // Pinned here: otherwise the compiler sinks the packs past the
+            // reference check (the rare path recomputes them) and keeps the
+            // 32 fp32 values alive across it, 20 more VGPRs.
+            asm volatile("" ::"v"(pk[4 * u + w4]));
           }
         return ls0 + ls1;
       };

@@ -15,7 +15,7 @@ constexpr int FWD_BR = 128;     // query rows per fp32 forward workgroup (== MAS
 // choices): FA_FWD16_LARGE_GRID (workgroups from which the d = 64 forward
 // takes its two-slot form; 0 = always, a huge value = never),
 // FA_BWD_WAVES_D64 (2 or 1), FA_BWD_WAVES_D128 (1 or 2), FA_FWD8_WAVES_D64
-// (3 or 4).
+// (4 or 3).
 #ifndef FA_FWD16_LARGE_GRID
 #define FA_FWD16_LARGE_GRID 2048
 #endif
@@ -26,7 +26,7 @@ constexpr int FWD_BR = 128;     // query rows per fp32 forward workgroup (== MAS
 #define FA_BWD_WAVES_D128 1
 #endif
 #ifndef FA_FWD8_WAVES_D64
-#define FA_FWD8_WAVES_D64 3
+#define FA_FWD8_WAVES_D64 4
 #endif
 // 16-bit forward: 64-key K/V tiles held in two LDS rings (K and V) of NS
 // slots each.  d = 64: NS = 3 (48 KiB, three workgroups per CU, copies issued
@@ -47,9 +47,9 @@ constexpr int dec_waves(int d) { return d == 64 ? 2 : 1; }
 constexpr int DEC_MAX_NQ = 16;  // queries per head the decode kernel holds (one MFMA column block)
 constexpr int DEC_SPLIT_ALIGN = 128;  // key-range lengths are multiples of 4 waves x 32 keys
 // FP8 forward: waves per SIMD (three-slot rings of 64-key E4M3 K and V^T
-// tiles: 24 KiB at d = 64, 48 KiB at d = 128).  The 16 registers that hold
-// -m for the score accumulators take d = 64 to 144 VGPRs (three waves); under
-// the four-wave cap of 128 the compiler spills 68 bytes per lane.
+// tiles: 24 KiB at d = 64, 48 KiB at d = 128).  d = 64 fits four waves in
+// 124-126 VGPRs with no spills (the E4M3 packs are pinned before the
+// reference check, so the 32 fp32 exponentials die there).
 constexpr int fwd8_waves(int d) { return d == 64 ? FA_FWD8_WAVES_D64 : 2; }
 constexpr int FWD_MAX_MASK_TILES = 2048;  // block-mask columns the forward caches (N <= 262144)
 
