@@ -59,9 +59,11 @@ using ic = std::integral_constant<int, V>;
 // 64-row Q / dO tiles plus their statistics through a 4-slot LDS ring, copies
 // issued two tiles ahead.
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
-__global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, dkdv_waves(D)) void bwd_dkdv_u_kernel(BwdParams p) {
   using VT = typename V8<T>::t;
-  constexpr int NW = 4, BC = NW * 32, QT = 64, NS = 4;
+  // Ring slots: four (copies two tiles ahead), or three (one tile ahead) when
+  // three workgroups share a CU's LDS.
+  constexpr int NW = 4, BC = NW * 32, QT = 64, NS = dkdv_waves(D) == 3 ? 3 : 4;
   constexpr int DS = D / 16, DB = D / 32, CPR = D / 8;
   constexpr int TILE = QT * D;                   // elements of one Q (or dO) tile
   constexpr int DMA_N = QT * CPR / 256;          // 16-byte copies per wave per tile
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdPara
   f32x16 s_odd, dp_odd, s_even, dp_even;
   VT pa_odd[2], ds_odd[2], pa_even[2], ds_even[2];
   if (iq[0] < i_end) {
-    if (iq[2] < i_end) wait_vmcnt<2 * OPS>();
+    if (NS == 4 && iq[2] < i_end) wait_vmcnt<2 * OPS>();
     else if (iq[1] < i_end) wait_vmcnt<OPS>();
     else wait_vmcnt<0>();
     wg_barrier();
@@ -338,16 +340,18 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdPara
   // constant slots need more registers than the occupancy allows).  MASKED
   // iterations apply the edge masks; the others are branch-free between
   // their two blocks.
-  int n = 0;
+  int sl = 0;  // slot of tile n
   auto iteration = [&](auto masked_c) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_c)::value;
-    const int SL = n & (NS - 1), SL1 = (n + 1) & (NS - 1);  // slots of tiles n, n+1
+    const int SL = sl, SL1 = sl == NS - 1 ? 0 : sl + 1;  // slots of tiles n, n+1
     const int i = iq[0], i1 = iq[1];
-    // Tile n+1 has landed once at most tile n+2's copies are in flight.
-    if (iq[2] < i_end) wait_vmcnt<OPS>();
+    // Tile n+1 has landed once at most tile n+2's copies are in flight (four
+    // slots; with three, tile n+2 is issued below).
+    if (NS == 4 && iq[2] < i_end) wait_vmcnt<OPS>();
     else wait_vmcnt<0>();
     wg_barrier();
-    if (iq[3] < i_end) issue(iq[3], (SL + 3) & (NS - 1));
+    // Tile n+NS-1 into the slot of tile n-1, which every wave has finished.
+    if (iq[NS - 1] < i_end) issue(iq[NS - 1], SL == 0 ? NS - 1 : SL - 1);
     // Units 2n+1 (second half of tile n) and 2n+2 (first half of tile n+1;
     // past the last tile it is masked whole and never used).
     if constexpr (MASKED) mask_unit(i * QT + 32, s_odd);
@@ -359,7 +363,7 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dkdv_u_kernel(BwdPara
 #pragma unroll
     for (int t = 0; t < NS - 1; ++t) iq[t] = iq[t + 1];
     iq[NS - 1] = iq[NS - 2] < i_end ? next_active(iq[NS - 2] + 1) : i_end;
-    ++n;
+    sl = SL1;
   };
   // Iterations needing no mask (units 2n+1, 2n+2 past the causal diagonal
   // and inside N) form one contiguous run: masked ones come before it

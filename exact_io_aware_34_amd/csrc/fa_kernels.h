@@ -40,6 +40,12 @@ constexpr int fwd16_waves(int d, int ns) { return d == 64 ? (ns == 3 ? 3 : 4) : 
 // d = 128 one wave holds K, V rows and fp32 dK, dV accumulators (512
 // registers) and its workgroup takes most of the CU's LDS.
 constexpr int bwd_u_waves(int d) { return d == 64 ? FA_BWD_WAVES_D64 : FA_BWD_WAVES_D128; }
+// dK/dV kernel: waves per SIMD at d = 64 may differ from the dQ kernel's
+// (three needs its three-slot ring, 51 KiB of LDS per workgroup).
+#ifndef FA_DKDV_WAVES_D64
+#define FA_DKDV_WAVES_D64 FA_BWD_WAVES_D64
+#endif
+constexpr int dkdv_waves(int d) { return d == 64 ? FA_DKDV_WAVES_D64 : bwd_u_waves(d); }
 // Decode: waves per SIMD (== workgroups per CU).  Each workgroup holds four
 // waves' two-slot rings of 32-key K and V tiles: 64 KiB at d = 64, 128 KiB at
 // d = 128.
