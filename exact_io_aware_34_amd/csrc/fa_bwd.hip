@@ -695,19 +695,27 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dq_u_kernel(BwdParams
 // most first, ties by index (with the causal flag only tiles on or below the
 // diagonal count).  The backward kernels take their tiles in this order, so
 // the longest workgroups start first and the shortest fill the tail.  One
-// workgroup; counts and ranks in LDS (n <= FWD_MAX_MASK_TILES).
+// workgroup of 16 waves; counts and ranks in LDS (n <= FWD_MAX_MASK_TILES).
 __global__ __launch_bounds__(1024) void sparse_order_kernel(const uint8_t* __restrict__ mask, int n,
                                                             int causal, int* __restrict__ qt_order,
                                                             int* __restrict__ kt_order) {
   __shared__ int row_n[FWD_MAX_MASK_TILES], col_n[FWD_MAX_MASK_TILES];
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    int rc = 0, cc = 0;
-    for (int t = 0; t < n; ++t) {
-      rc += (mask[(size_t)i * n + t] != 0) && (!causal || t <= i);
-      cc += (mask[(size_t)t * n + i] != 0) && (!causal || t >= i);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < n; i += 1024) col_n[i] = 0;
+  __syncthreads();
+  // Tile (r, c) counts for row r and column c when it is set (and, causal,
+  // c <= r).  A wave reads one mask row at a time, 64 columns per step: the
+  // row count is the popcount of the step ballots, the column counts LDS
+  // atomic adds.
+  for (int r = wave; r < n; r += 16) {
+    int rc = 0;
+    for (int c0 = 0; c0 < n; c0 += 64) {
+      const int c = c0 + lane;
+      const bool vis = c < n && mask[(size_t)r * n + c] != 0 && (!causal || c <= r);
+      rc += __popcll(__builtin_amdgcn_ballot_w64(vis));
+      if (vis) atomicAdd(&col_n[c], 1);
     }
-    row_n[i] = rc;
-    col_n[i] = cc;
+    if (lane == 0) row_n[r] = rc;
   }
   __syncthreads();
   for (int i = threadIdx.x; i < n; i += blockDim.x) {

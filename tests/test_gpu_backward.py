@@ -170,7 +170,8 @@ def test_backward_row_statistics(fa, B, H, N, d, dtype, causal, sparse, dropout_
     assert (lse2[fin] - want[fin]).abs().max().item() <= 1e-6 * max(1.0, want[fin].abs().max().item())
 
 
-@pytest.mark.parametrize("N,causal", [(1000, False), (700, True), (4100, False)])
+@pytest.mark.parametrize("N,causal", [(1000, False), (700, True), (4100, False), (9000, True),
+                                      (16400, False)])
 def test_block_sparse_work_order(fa, N, causal):
     """With a block mask the backward ranks the mask's rows (query tiles) and
     columns (key tiles) by visible-tile count, most first, ties by index, into
