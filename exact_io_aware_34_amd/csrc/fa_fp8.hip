@@ -416,7 +416,7 @@ __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
             // Pinned here: otherwise the compiler sinks the packs past the
             // reference check (the rare path recomputes them) and keeps the
             // 32 fp32 values alive across it, 20 more VGPRs.
-            asm volatile("" ::"v"(pk[4 * u + w4]));
+            if constexpr (FA_FP8_PIN_PACKS) asm volatile("" ::"v"(pk[4 * u + w4]));
           }
         return ls0 + ls1;
       };

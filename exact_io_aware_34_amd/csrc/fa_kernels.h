@@ -15,7 +15,7 @@ constexpr int FWD_BR = 128;     // query rows per fp32 forward workgroup (== MAS
 // choices): FA_FWD16_LARGE_GRID (workgroups from which the d = 64 forward
 // takes its two-slot form; 0 = always, a huge value = never),
 // FA_BWD_WAVES_D64 (2 or 1), FA_BWD_WAVES_D128 (1 or 2), FA_FWD8_WAVES_D64
-// (4 or 3).
+// (4 or 3), FA_FP8_PIN_PACKS and FA_DKDV_WAVES_D64 (below).
 #ifndef FA_FWD16_LARGE_GRID
 #define FA_FWD16_LARGE_GRID 2048
 #endif
@@ -27,6 +27,11 @@ constexpr int FWD_BR = 128;     // query rows per fp32 forward workgroup (== MAS
 #endif
 #ifndef FA_FWD8_WAVES_D64
 #define FA_FWD8_WAVES_D64 4
+#endif
+// FP8 forward: E4M3 packs pinned before the reference check (1) or left to
+// the compiler (0: 144 VGPRs at d = 64, three waves per SIMD).
+#ifndef FA_FP8_PIN_PACKS
+#define FA_FP8_PIN_PACKS 1
 #endif
 // 16-bit forward: 64-key K/V tiles held in two LDS rings (K and V) of NS
 // slots each.  d = 64: NS = 3 (48 KiB, three workgroups per CU, copies issued
