@@ -206,8 +206,8 @@ def time_passes(fa, w, tensors, mask, steps, warmup, dropout_p=0.0, seed=0):
     # Without dropout fa.forward splits the key range of grids too small to
     # fill the GPU (the library's choice); its workspace is allocated here.
     ws_f = None
-    if not dropout_p and fa.forward_splits(w.B, w.H, w.N, w.d, 0) > 1:
-        ws_f = torch.empty(fa.forward_split_workspace_size(w.B, w.H, w.N, w.d, 0),
+    if not dropout_p and fa.forward_splits(w.B, w.H, w.N, w.d, 0, q.dtype) > 1:
+        ws_f = torch.empty(fa.forward_split_workspace_size(w.B, w.H, w.N, w.d, 0, q.dtype),
                            dtype=torch.uint8, device=q.device)
 
     def step(ev=None):
@@ -345,8 +345,8 @@ def bench_split(fa, w, tensors, mask, steps, warmup, fwd_ms):
     plain forward grid is too small to fill the GPU."""
     import torch
     q, k, v, _, o, lse, _, _ = tensors
-    n = fa.forward_splits(w.B, w.H, w.N, w.d, 0)
-    ws = torch.empty(max(1, fa.forward_split_workspace_size(w.B, w.H, w.N, w.d, 0)),
+    n = fa.forward_splits(w.B, w.H, w.N, w.d, 0, q.dtype)
+    ws = torch.empty(max(1, fa.forward_split_workspace_size(w.B, w.H, w.N, w.d, 0, q.dtype)),
                      dtype=torch.uint8, device=q.device)
     stream = torch.cuda.current_stream()
 
@@ -518,7 +518,7 @@ def bench_other(fa, name, steps, warmup):
     out = {"B": w.B, "H": w.H, "N": w.N, "d": w.d, "dtype": w.dtype, "causal": w.causal,
            "block_sparse": w.sparse, "steps": steps, "warmup": warmup,
            "work_fraction": round(work_fraction(w, inputs["mask"]), 5),
-           "forward_key_runs": fa.forward_splits(w.B, w.H, w.N, w.d, 0)}
+           "forward_key_runs": fa.forward_splits(w.B, w.H, w.N, w.d, 0, W.TORCH_DTYPES[w.dtype])}
     out.update(pass_summary(w, inputs["mask"], fwd_ms, bwd_ms, wall, steps))
     if w.sparse:
         out["skip_efficiency"] = skip_efficiency(fa, w, tensors, mask, steps, fwd_ms, bwd_ms)
@@ -571,7 +571,7 @@ def main():
     out.update({k_: v_ for k_, v_ in summary.items() if k_ not in ("value", "ms_per_step")})
     if w.sparse:
         out["skip_efficiency"] = skip_efficiency(fa, w, tensors, mask, args.steps, fwd_ms, bwd_ms)
-    if fa.forward_splits(B, H, N, d, 0) > 1:
+    if fa.forward_splits(B, H, N, d, 0, W.TORCH_DTYPES[w.dtype]) > 1:
         out["split_forward"] = bench_split(fa, w, tensors, mask, args.steps, args.warmup,
                                            mean(fwd_ms))
     if not args.no_dropout and w.dtype in ("bf16", "f16") and w.backward:

@@ -228,19 +228,27 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
 // smaller than one full round of workgroups (768 at d = 64: three per CU;
 // 512 at d = 128: two): enough (query tile, run) workgroups for one round,
 // with runs of at least ten 64-key tiles.  In a sweep of the count (1..32)
-// on five shapes (one to four heads, N = 4096..16384, d = 64 and 128, causal
-// and not) this choice was the fastest count on every one; runs shorter than
-// ~10 tiles spend most of their time filling and draining the copy
-// pipeline.  An explicit count is capped at the number of 64-key tiles.
-int forward_split_count(int B, int H, int N, int d, int n_splits) {
+// on five 16-bit shapes (one to four heads, N = 4096..16384, d = 64 and 128,
+// causal and not) this choice was the fastest count on every one; runs
+// shorter than ~10 tiles spend most of their time filling and draining the
+// copy pipeline.  An fp32 tile costs the matrix cores ~16 times as long, so
+// for fp32 inputs two tiles per run already cover the fill and one
+// workgroup per CU (256) is enough: one head at d = 64 took 91.6 us in one
+// run and 26 us in eight at N = 1024, 29.4 us in one and 22.5 us in two at
+// N = 256, and 77-80 us in 6 to 24 runs at N = 4096.  An explicit count is
+// capped at the number of 64-key tiles.
+int forward_split_count(int B, int H, int N, int d, int n_splits, int dtype) {
   if (B < 1 || H < 1 || N < 1 || n_splits < 0 || (d != 64 && d != 128)) return 0;
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return 0;
   const long long n_kt = (N + 63) / 64;
   const long long wgs = (long long)B * H * ((N + 127) / 128);
   const long long round = d == 64 ? 768 : 512;
+  const long long target = dtype == FA_F32 ? 256 : round;
+  const long long min_run = dtype == FA_F32 ? 2 : 10;
   long long n = n_splits;
   if (n == 0) {
     n = 1;
-    if (wgs < round) n = std::min((round + wgs - 1) / wgs, std::max(1LL, n_kt / 10));
+    if (wgs < round) n = std::min((target + wgs - 1) / wgs, std::max(1LL, n_kt / min_run));
   }
   n = std::min(n, std::min(n_kt, (long long)kMaxForwardSplits));
   return (int)std::max(1LL, n);
@@ -254,12 +262,12 @@ size_t forward_split_part_bytes(int B, int H, int N, int d, int n) {
 
 extern "C" {
 
-int fa_forward_splits(int B, int H, int N, int d, int n_splits) {
-  return forward_split_count(B, H, N, d, n_splits);
+int fa_forward_splits(int B, int H, int N, int d, int n_splits, int dtype) {
+  return forward_split_count(B, H, N, d, n_splits, dtype);
 }
 
-size_t fa_forward_split_workspace_size(int B, int H, int N, int d, int n_splits) {
-  const int n = forward_split_count(B, H, N, d, n_splits);
+size_t fa_forward_split_workspace_size(int B, int H, int N, int d, int n_splits, int dtype) {
+  const int n = forward_split_count(B, H, N, d, n_splits, dtype);
   if (n <= 1) return 0;
   return forward_split_part_bytes(B, H, N, d, n) + pad256((size_t)B * H * n * N * sizeof(float));
 }
@@ -271,7 +279,7 @@ int fa_forward_split(const void* q, const void* k, const void* v, void* o, float
   if (n_splits < 0) return FA_ERR_INVALID_ARG;
   const int rc = check_common(B, H, N, d, scale, dtype);
   if (rc != FA_OK) return rc;
-  const int n = forward_split_count(B, H, N, d, n_splits);
+  const int n = forward_split_count(B, H, N, d, n_splits, dtype);
   if (n <= 1)
     return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, dtype, false, 0.f,
                         0, 0, nullptr, stream);
@@ -284,7 +292,7 @@ int fa_forward_split(const void* q, const void* k, const void* v, void* o, float
   const long long rows = (long long)B * H * n * N;
   if (rows > (1LL << 31) - 1 || (long long)B * H * n * ((N + 127) / 128) > (1LL << 31) - 1)
     return FA_ERR_UNSUPPORTED;
-  const size_t need = fa_forward_split_workspace_size(B, H, N, d, n_splits);
+  const size_t need = fa_forward_split_workspace_size(B, H, N, d, n_splits, dtype);
   if (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < need)
     return FA_ERR_WORKSPACE;
   fa::FwdParams p{};

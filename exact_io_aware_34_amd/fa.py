@@ -59,9 +59,9 @@ _lib.fa_dropout_mask.restype = _i
 _lib.fa_forward_split.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _i, _i, _vp,
                                   ctypes.c_size_t, _vp]
 _lib.fa_forward_split.restype = _i
-_lib.fa_forward_splits.argtypes = [_i, _i, _i, _i, _i]
+_lib.fa_forward_splits.argtypes = [_i, _i, _i, _i, _i, _i]
 _lib.fa_forward_splits.restype = _i
-_lib.fa_forward_split_workspace_size.argtypes = [_i, _i, _i, _i, _i]
+_lib.fa_forward_split_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i]
 _lib.fa_forward_split_workspace_size.restype = ctypes.c_size_t
 _lib.fa_decode_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _i,
                                    _vp]
@@ -146,18 +146,25 @@ def default_scale(d: int) -> float:
     return float(torch.tensor(d ** -0.5, dtype=torch.float32))
 
 
-def forward_splits(B, H, N, d, n_splits=0) -> int:
-    """Number of key runs fa_forward_split uses for this shape (0 on bad input)."""
-    return int(_lib.fa_forward_splits(B, H, N, d, n_splits))
+def _dtype_code(dtype):
+    if dtype not in DTYPE_CODES:
+        raise ValueError(f"unsupported dtype {dtype}")
+    return DTYPE_CODES[dtype]
 
 
-def fa_forward_splits_used(B, H, N, d, n_splits) -> int:
+def forward_splits(B, H, N, d, n_splits=0, dtype=torch.bfloat16) -> int:
+    """Number of key runs fa_forward_split uses for this shape and input dtype
+    (0 on bad input)."""
+    return int(_lib.fa_forward_splits(B, H, N, d, n_splits, _dtype_code(dtype)))
+
+
+def fa_forward_splits_used(B, H, N, d, n_splits, dtype=torch.bfloat16) -> int:
     """Key runs fa_forward_split would use (1 when the plain forward runs)."""
-    return int(_lib.fa_forward_splits(B, H, N, d, n_splits)) if n_splits != 1 else 1
+    return forward_splits(B, H, N, d, n_splits, dtype) if n_splits != 1 else 1
 
 
-def forward_split_workspace_size(B, H, N, d, n_splits=0) -> int:
-    return int(_lib.fa_forward_split_workspace_size(B, H, N, d, n_splits))
+def forward_split_workspace_size(B, H, N, d, n_splits=0, dtype=torch.bfloat16) -> int:
+    return int(_lib.fa_forward_split_workspace_size(B, H, N, d, n_splits, _dtype_code(dtype)))
 
 
 def forward(q, k, v, causal=False, scale=None, block_mask=None, out=None, lse=None,
@@ -184,8 +191,8 @@ def forward(q, k, v, causal=False, scale=None, block_mask=None, out=None, lse=No
     drop = bool(dropout_p) or o_acc is not None
     if drop and n_splits not in (0, 1):
         raise ValueError("split key runs are not offered with dropout")
-    if not drop and fa_forward_splits_used(B, H, N, d, n_splits) > 1:
-        ws_bytes = forward_split_workspace_size(B, H, N, d, n_splits)
+    if not drop and fa_forward_splits_used(B, H, N, d, n_splits, q.dtype) > 1:
+        ws_bytes = forward_split_workspace_size(B, H, N, d, n_splits, q.dtype)
         if workspace is None and ws_bytes > 0:
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
         nbytes = _check_workspace(workspace)

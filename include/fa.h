@@ -90,7 +90,9 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
  * n_splits = 0 lets the library choose (fa_forward_splits()): one run unless
  * the plain grid (B*H*ceil(N/128) workgroups) is smaller than one round of
  * the GPU (768 workgroups at d = 64, 512 at d = 128), then enough runs for
- * one round, with at least ten 64-key tiles per run.  An explicit n_splits is
+ * one round, with at least ten 64-key tiles per run (for FA_F32 inputs, whose
+ * tiles take the matrix cores far longer: enough runs for one workgroup per
+ * CU, at least two tiles each).  An explicit n_splits is
  * capped at ceil(N / 64) and at 64.  With one run this is fa_forward and no
  * workspace is used.  `workspace` (at least
  * fa_forward_split_workspace_size() bytes, 256-byte aligned, caller-owned,
@@ -104,12 +106,13 @@ int fa_forward_split(const void* q, const void* k, const void* v, void* o, float
                      const uint8_t* block_mask, int dtype, int n_splits, void* workspace,
                      size_t workspace_bytes, void* stream);
 
-/* Number of key runs fa_forward_split uses for this shape (0 on bad input). */
-int fa_forward_splits(int B, int H, int N, int d, int n_splits);
+/* Number of key runs fa_forward_split uses for this shape and input dtype
+ * (0 on bad input). */
+int fa_forward_splits(int B, int H, int N, int d, int n_splits, int dtype);
 
 /* Bytes of workspace fa_forward_split needs (0 when it uses one run or on bad
  * input). */
-size_t fa_forward_split_workspace_size(int B, int H, int N, int d, int n_splits);
+size_t fa_forward_split_workspace_size(int B, int H, int N, int d, int n_splits, int dtype);
 
 /* Bytes of device workspace fa_backward needs for this shape (0 on bad input):
  * two fp32 values per (b, h, row), each array padded to 256 bytes, then two
@@ -315,8 +318,9 @@ size_t fa_forward_fp8_workspace_size(int B, int H, int N, int d);
 const char* fa_status_string(int status);
 
 /* Library ABI version (this header: 4; 2 added fa_forward_split*, 3 the fp32
- * output o_acc of the dropout calls, 4 power-of-two FP8 block scales and the
- * scale argument of fa_fp8_prepare). */
+ * output o_acc of the dropout calls, 4 power-of-two FP8 block scales, the
+ * scale argument of fa_fp8_prepare and the dtype argument of
+ * fa_forward_splits and fa_forward_split_workspace_size). */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

@@ -44,8 +44,8 @@ def lib():
     L.fa_dropout_mask.argtypes = [i, i, i, f, u64, u32, vp, vp]
     L.fa_forward_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, i, vp,
                                    ctypes.c_size_t, vp]
-    L.fa_forward_splits.argtypes = [i] * 5
-    L.fa_forward_split_workspace_size.argtypes = [i] * 5
+    L.fa_forward_splits.argtypes = [i] * 6
+    L.fa_forward_split_workspace_size.argtypes = [i] * 6
     L.fa_forward_split_workspace_size.restype = ctypes.c_size_t
     return L
 
@@ -264,7 +264,8 @@ def test_dropout_validation(lib):
 
 
 def test_forward_split_choice(lib):
-    S = lib.fa_forward_splits
+    def S(B, H, N, d, n, dtype=2):                # default: bf16 inputs
+        return lib.fa_forward_splits(B, H, N, d, n, dtype)
     # Automatic: one run once the plain grid fills a round (768 workgroups at
     # d = 64, 512 at d = 128).
     assert S(4, 12, 8192, 64, 0) == 1          # 3072 query tiles
@@ -278,6 +279,14 @@ def test_forward_split_choice(lib):
     assert S(1, 2, 4096, 128, 0) == 6          # 64 tiles -> 8 wanted, 64 key tiles / 10
     assert S(1, 1, 256, 64, 0) == 1            # 4 key tiles
     assert S(1, 1, 1000, 64, 0) == 1           # 16 key tiles: one run of >= 10
+    assert S(1, 1, 1000, 64, 0, 1) == 1        # fp16: the same rule
+    # fp32 inputs: 256 workgroups wanted, runs of >= 2 key tiles
+    assert S(1, 1, 256, 64, 0, 0) == 2         # 4 key tiles
+    assert S(1, 1, 1000, 64, 0, 0) == 8        # 16 key tiles, 8 query tiles -> 32 wanted
+    assert S(1, 1, 4096, 64, 0, 0) == 8        # 32 query tiles -> 8 wanted
+    assert S(1, 4, 8192, 64, 0, 0) == 1        # 256 query tiles
+    assert S(4, 12, 8192, 64, 0, 0) == 1       # full grid
+    assert S(1, 1, 100, 64, 0, 0) == 1         # 2 key tiles
     # Explicit counts are capped at the key tiles and at 64.
     assert S(1, 1, 300, 64, 9) == 5
     assert S(1, 1, 1 << 16, 64, 100) == 64
@@ -286,15 +295,19 @@ def test_forward_split_choice(lib):
     assert S(0, 1, 10, 64, 0) == 0
     assert S(1, 1, 10, 96, 0) == 0
     assert S(1, 1, 10, 64, -1) == 0
+    assert S(1, 1, 10, 64, 0, 7) == 0          # unknown dtype
 
 
 def test_forward_split_workspace_size(lib):
-    W = lib.fa_forward_split_workspace_size
+    def W(B, H, N, d, n, dtype=2):
+        return lib.fa_forward_split_workspace_size(B, H, N, d, n, dtype)
     assert W(4, 12, 8192, 64, 0) == 0          # one run
     assert W(1, 1, 300, 64, 1) == 0
     # 6 runs of 4096 rows x 64 fp32, then 6 x 4096 fp32
     assert W(1, 1, 4096, 64, 0) == 6 * 4096 * 64 * 4 + 6 * 4096 * 4
     assert W(1, 2, 300, 128, 3) == 2 * 3 * 300 * 128 * 4 + (-(-2 * 3 * 300 * 4 // 256)) * 256
+    assert W(1, 1, 256, 64, 0, 0) == 2 * 256 * 64 * 4 + 2 * 256 * 4      # fp32: 2 runs
+    assert W(1, 1, 256, 64, 0, 9) == 0
 
 
 def fsplit(lib, q=FAKE, lse=FAKE, B=1, H=1, N=4096, d=64, scale=0.125, dtype=2, n=4, ws=FAKE,
@@ -314,7 +327,7 @@ def test_forward_split_validation(lib):
     assert fsplit(lib, d=80) == -2
     assert fsplit(lib, ws=None) == -3
     assert fsplit(lib, ws=MISALIGNED) == -3
-    need = lib.fa_forward_split_workspace_size(1, 1, 4096, 64, 4)
+    need = lib.fa_forward_split_workspace_size(1, 1, 4096, 64, 4, 2)
     assert need > 0 and fsplit(lib, ws_bytes=need - 1) == -3
 
 

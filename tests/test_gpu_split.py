@@ -83,13 +83,15 @@ def test_split_counts_agree(fa):
         assert_close(f"lse n={n}", f64(ln), f64(l1), LSE_TOL)
 
 
-@pytest.mark.parametrize("name", ["dense_n4096_d64_bf16", "dense_n4096_d64_f32"])
+@pytest.mark.parametrize("name", ["dense_n4096_d64_bf16", "dense_n4096_d64_f32",
+                                  "dense_n256_d64_f32"])
 def test_split_named_small_workload(fa, name):
-    """The single-head N = 4096 workloads (32 query tiles) in the
-    configuration the benchmark times for them (library-chosen run count)."""
+    """The single-head workloads (32 query tiles at N = 4096, two at N = 256
+    in fp32) in the configuration the benchmark times for them
+    (library-chosen run count)."""
     w = W.make(name)
     wl = w["workload"]
-    assert fa.forward_splits(wl.B, wl.H, wl.N, wl.d, 0) > 1
+    assert fa.forward_splits(wl.B, wl.H, wl.N, wl.d, 0, w["q"].dtype) > 1
     o, lse = run_split(fa, w["q"], w["k"], w["v"], w["scale"], w["causal"], w["mask"], 0)
     (ro, rl), = oracle_forward_heads(w["q"], w["k"], w["v"], w["scale"], w["causal"],
                                      w["mask"], [(0, 0)])
