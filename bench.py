@@ -18,7 +18,9 @@ The other workloads (long-context fp16, block-sparse d = 128, and the
 single-head N = 4096 bf16 / fp32 and N = 256 fp32 forwards) are timed the
 same way after the headline steps and reported in the `workloads` object
 (the single-head forwards through the library's default, which splits their
-key ranges over more workgroups).
+key ranges over more workgroups); each 16-bit forward + backward entry also
+carries the FP8 forward on the same inputs (`fp8`: call time with the
+preparation, its ratio to the 16-bit forward).
 
 The decode path (fa_decode: a few queries against a long cached K/V history)
 is timed after the steps on its own workload and reported in the `decode`
@@ -522,6 +524,12 @@ def bench_other(fa, name, steps, warmup):
     out.update(pass_summary(w, inputs["mask"], fwd_ms, bwd_ms, wall, steps))
     if w.sparse:
         out["skip_efficiency"] = skip_efficiency(fa, w, tensors, mask, steps, fwd_ms, bwd_ms)
+    if w.backward and w.dtype in ("bf16", "f16"):
+        # The FP8 forward on the same inputs (rotation + quantisation included).
+        f8 = bench_fp8(fa, w, inputs, tensors, mask, steps, warmup, 0, False)
+        out["fp8"] = {k_: f8[k_] for k_ in ("ms", "ms_median_min", "prep_ms", "tflops")}
+        out["fp8"]["frac_fp8_peak"] = f8["roofline"]["frac"]
+        out["fp8"]["vs_16bit_forward"] = round(sum(fwd_ms) / len(fwd_ms) / f8["ms"], 3)
     del tensors, mask
     torch.cuda.empty_cache()
     return out
