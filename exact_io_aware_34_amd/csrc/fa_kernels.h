@@ -15,7 +15,8 @@ constexpr int FWD_BR = 128;     // query rows per fp32 forward workgroup (== MAS
 // choices): FA_FWD16_LARGE_GRID (workgroups from which the d = 64 forward
 // takes its two-slot form; 0 = always, a huge value = never),
 // FA_BWD_WAVES_D64 (2 or 1), FA_BWD_WAVES_D128 (1 or 2), FA_FWD8_WAVES_D64
-// (4 or 3), FA_FP8_PIN_PACKS and FA_DKDV_WAVES_D64 (below).
+// (4 or 3), FA_FWD8_WAVES_D128, FA_FP8_PIN_PACKS and FA_DKDV_WAVES_D64
+// (below).
 #ifndef FA_FWD16_LARGE_GRID
 #define FA_FWD16_LARGE_GRID 2048
 #endif
@@ -60,8 +61,12 @@ constexpr int DEC_SPLIT_ALIGN = 128;  // key-range lengths are multiples of 4 wa
 // FP8 forward: waves per SIMD (three-slot rings of 64-key E4M3 K and V^T
 // tiles: 24 KiB at d = 64, 48 KiB at d = 128).  d = 64 fits four waves in
 // 124-126 VGPRs with no spills (the E4M3 packs are pinned before the
-// reference check, so the 32 fp32 exponentials die there).
-constexpr int fwd8_waves(int d) { return d == 64 ? FA_FWD8_WAVES_D64 : 2; }
+// reference check, so the 32 fp32 exponentials die there); d = 128 fits
+// three in 167-168 (147 KiB of LDS for three workgroups per CU).
+#ifndef FA_FWD8_WAVES_D128
+#define FA_FWD8_WAVES_D128 3
+#endif
+constexpr int fwd8_waves(int d) { return d == 64 ? FA_FWD8_WAVES_D64 : FA_FWD8_WAVES_D128; }
 constexpr int FWD_MAX_MASK_TILES = 2048;  // block-mask columns the forward caches (N <= 262144)
 
 struct FwdParams {
