@@ -246,27 +246,44 @@ def test_fp8_rotation_helps_with_outliers(fa):
     assert min(ratios_o) > 1.0 and np.mean(ratios_o) > 1.05
 
 
-def test_fp8_full_size_sampled(fa):
-    """The headline geometry (B4 H12 N8192 d64 causal bf16) through the FP8
-    path, sampled heads and rows against the emulation and exact attention."""
-    inp = W.make(W.HEADLINE)
+FULL_SIZE = [
+    # workload, sampled (b, h), sampled rows
+    ("causal_b4h12_n8192_d64_bf16", [(0, 0), (3, 11), (2, 5)],
+     [0, 1, 63, 64, 127, 128, 4095, 4096, 8000, 8191]),
+    ("causal_b1h12_n23400_d64_f16", [(0, 0), (0, 11)], [0, 127, 128, 11000, 23295, 23399]),
+    ("sparse_b2h16_n16384_d128_bf16", [(0, 0), (1, 15)], [0, 200, 5000, 9999, 16383]),
+]
+
+
+@pytest.mark.parametrize("name,heads,rows", FULL_SIZE)
+def test_fp8_full_size_sampled(fa, name, heads, rows):
+    """The full-size workloads (headline, long-context fp16, block-sparse
+    d = 128) through the FP8 path, sampled heads and rows against the
+    emulation and exact attention."""
+    inp = W.make(name)
     w = inp["workload"]
     signs = W.draw_rotation_signs(w.d, seed=7)
+    mask = inp["mask"]
     o, lse = fa.forward_fp8(inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(),
-                            signs=signs.cuda(), causal=True, scale=w.scale)
+                            signs=signs.cuda(), causal=w.causal, scale=w.scale,
+                            block_mask=None if mask is None else mask.cuda())
     torch.cuda.synchronize()
-    rows = np.array([0, 1, 63, 64, 127, 128, 4095, 4096, 8000, 8191])
+    rows = np.array(rows)
     sg = signs.numpy().astype(np.float64)
-    for b, h in [(0, 0), (3, 11), (2, 5)]:
+    mnp = None if mask is None else mask.numpy()
+    for b, h in heads:
         a = [f64(inp[n][b, h]) for n in ("q", "k", "v")]
-        eo, el, terms = oracle.fp8_forward_head(*a, w.scale, True, None, sg, rows=rows,
+        eo, el, terms = oracle.fp8_forward_head(*a, w.scale, w.causal, mnp, sg, rows=rows,
                                                 terms=True)
-        xo, xl = oracle.forward_head(*a, w.scale, causal=True, rows=rows)
+        xo, xl = oracle.forward_head(*a, w.scale, causal=w.causal, block_mask=mnp, rows=rows)
         ko, kl = f64(o[b, h])[rows], lse[b, h].cpu().double().numpy()[rows]
         assert np.all(np.abs(ko - eo) <= o_bound(terms, eo)), f"[{b},{h}] element bound"
         err_k, err_e, dist = _rms(ko - xo), _rms(eo - xo), _rms(ko - eo)
-        print(f"full [{b},{h}] rms(kernel-exact)={err_k:.3e} rms(emul-exact)={err_e:.3e} "
-              f"rms(kernel-emul)={dist:.3e} max|lse-emul|={np.abs(kl - el).max():.3e}", flush=True)
+        fin = np.isfinite(el)
+        lse_d = float(np.abs(kl[fin] - el[fin]).max(initial=0.0))
+        print(f"full {name} [{b},{h}] rms(kernel-exact)={err_k:.3e} rms(emul-exact)={err_e:.3e} "
+              f"rms(kernel-emul)={dist:.3e} max|lse-emul|={lse_d:.3e}", flush=True)
+        assert np.array_equal(np.isneginf(kl), np.isneginf(el))
         assert err_k <= 1.25 * err_e + 2e-4
         assert dist <= 0.75 * err_e + 2e-4
-        assert np.abs(kl - el).max() <= 2e-3
+        assert lse_d <= 2e-3
