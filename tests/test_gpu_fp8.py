@@ -28,7 +28,11 @@
     reference (2^-12 of the sum of absolute products plus the row's largest
     such sum), P by that relative amount; the P V accumulation adds 2^-11
     relative; the 16-bit output rounding 2^-8 of |o|;
-  - lse to 2e-3 (same codes; measured ~3e-5);
+  - lse to 2e-3 plus the same score allowance carried into the
+    logsumexp: ln 2 * sum_j (P_ij / l_i) delta_ij (lse moves by the
+    P-weighted mean of the score errors; measured ~3e-5 on N(0, 1) rows, up
+    to ~2.4e-3 on rows concentrated on one key with scores near 110 in
+    base 2);
   - in RMS, the kernel's error against exact attention at most 1.25x the
     method's (the emulation's) + 2e-4, and its distance from the emulation at
     most 0.75x that error + 2e-4 (measured: 0.99-1.02x and 0.2-0.6x);
@@ -161,6 +165,14 @@ def o_bound(t, o_ref, rows=None):
     return bound + 2.0 ** -8 * np.abs(o_ref) + 1e-6
 
 
+def lse_bound(t):
+    """Bound on |lse_kernel - lse_emulation| per row (module docstring)."""
+    delta = 2.0 ** -12 * (t["s_abs"] + t["s_abs"].max(axis=1, keepdims=True)) + 2.0 ** -20
+    with np.errstate(invalid="ignore", divide="ignore"):
+        w = (t["p"] * delta).sum(axis=1) / t["l"]
+    return 2e-3 + np.log(2.0) * np.where(np.isfinite(w), w, 0.0)
+
+
 def holed_mask(N, seed):
     t = -(-N // 128)
     g = torch.Generator().manual_seed(seed)
@@ -214,15 +226,42 @@ def test_fp8_forward(fa, B, H, N, d, dtype, causal, mask_kind, rotated):
             dist = _rms(o[b, h] - eo)
             fin = np.isfinite(el)
             lse_d = float(np.abs(lse[b, h][fin] - el[fin]).max(initial=0.0))
+            lse_x = float((np.abs(lse[b, h][fin] - el[fin]) - lse_bound(terms)[fin])
+                          .max(initial=-1.0))
             print(f"[{b},{h}] rms(kernel-exact)={err_k:.3e} rms(emul-exact)={err_e:.3e} "
                   f"rms(kernel-emul)={dist:.3e} max|o-emul|={np.abs(o[b, h] - eo).max():.3e} "
                   f"max|lse-emul|={lse_d:.3e} rms(o)={_rms(xo):.3e}", flush=True)
             assert np.array_equal(np.isneginf(lse[b, h]), np.isneginf(el))
             assert err_k <= 1.25 * err_e + 2e-4
             assert dist <= 0.75 * err_e + 2e-4
-            assert lse_d <= 2e-3
+            assert lse_x <= 0, f"[{b},{h}] lse over its bound by {lse_x:.3e}"
     if mask_kind == "holed":
         assert np.all(o[:, :, :128] == 0) and np.all(np.isneginf(lse[:, :, :128]))
+
+
+@pytest.mark.parametrize("d,causal", [(64, True), (128, False)])
+def test_fp8_peaked_rows(fa, d, causal):
+    """Scores far apart (scale 1, Q doubled): softmax rows concentrate on few
+    keys, a query's reference moves often and most P underflow in E4M3.  The
+    kernel must stay inside the same element-wise bound and lse tolerance
+    against the emulation."""
+    B, H, N = 1, 2, 700
+    q, k, v, _ = W.draw_qkvdo(B, H, N, d, "bf16", seed=17 + d)
+    q = (q.float() * 2).to(torch.bfloat16)
+    signs = W.draw_rotation_signs(d, seed=9)
+    sc = 1.0
+    o, lse = fa.forward_fp8(q.cuda(), k.cuda(), v.cuda(), signs=signs.cuda(), causal=causal,
+                            scale=sc)
+    torch.cuda.synchronize()
+    sg = signs.numpy().astype(np.float64)
+    for h in range(H):
+        a = [f64(t[0, h]) for t in (q, k, v)]
+        eo, el, terms = oracle.fp8_forward_head(*a, sc, causal, None, sg, terms=True)
+        ko, kl = f64(o[0, h]), lse[0, h].cpu().double().numpy()
+        excess = np.abs(ko - eo) - o_bound(terms, eo)
+        assert excess.max() <= 0, f"[{h}] over the bound by {excess.max():.3e}"
+        excess = np.abs(kl - el) - lse_bound(terms)
+        assert excess.max() <= 0, f"[{h}] lse over its bound by {excess.max():.3e}"
 
 
 def test_fp8_rotation_helps_with_outliers(fa):
@@ -281,9 +320,10 @@ def test_fp8_full_size_sampled(fa, name, heads, rows):
         err_k, err_e, dist = _rms(ko - xo), _rms(eo - xo), _rms(ko - eo)
         fin = np.isfinite(el)
         lse_d = float(np.abs(kl[fin] - el[fin]).max(initial=0.0))
+        lse_x = float((np.abs(kl[fin] - el[fin]) - lse_bound(terms)[fin]).max(initial=-1.0))
         print(f"full {name} [{b},{h}] rms(kernel-exact)={err_k:.3e} rms(emul-exact)={err_e:.3e} "
               f"rms(kernel-emul)={dist:.3e} max|lse-emul|={lse_d:.3e}", flush=True)
         assert np.array_equal(np.isneginf(kl), np.isneginf(el))
         assert err_k <= 1.25 * err_e + 2e-4
         assert dist <= 0.75 * err_e + 2e-4
-        assert lse_d <= 2e-3
+        assert lse_x <= 0, f"[{b},{h}] lse over its bound by {lse_x:.3e}"
