@@ -44,6 +44,7 @@ from .attention import (  # noqa: F401
     backward,
     backward_head,
     backward_head_sampled,
+    backward_head_terms,
     rowsum_do_o,
 )
 from .decode import (  # noqa: F401

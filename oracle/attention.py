@@ -121,6 +121,20 @@ def backward_head(q, k, v, do, scale, causal=False, block_mask=None,
     return dq, dk, dv
 
 
+def backward_head_terms(q, k, v, do, scale, causal=False, block_mask=None,
+                        mask_block=MASK_BLOCK):
+    """One head's intermediate quantities of backward_head, whole (N x N):
+    {"p": P, "ds": dS, "lse": lse, "o": o}, by the same definitions.  Tests
+    bound a kernel's rounding error with them; small N only."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    n = k.shape[0]
+    s = scale * (q @ k.T)
+    p, lse = _row_softmax(s, allowed(np.arange(q.shape[0]), n, causal, block_mask, mask_block))
+    o = p @ v
+    ds = p * (do @ v.T - rowsum_do_o(do, o)[:, None])
+    return {"p": p, "ds": ds, "lse": lse, "o": o}
+
+
 def backward_head_sampled(q, k, v, do, scale, causal=False, block_mask=None, q_rows=(),
                           k_cols=(), mask_block=MASK_BLOCK, chunk=512):
     """One head's dq at query rows `q_rows` and dk, dv at key rows `k_cols`.

@@ -107,3 +107,65 @@ def oracle_backward_sampled(q, k, v, do, scale, causal, mask, samples, workers=1
                 os.environ.pop(key, None)
             else:
                 os.environ[key] = val
+
+
+# Element-wise rounding bounds for the 16-bit (and fp32) kernels, from their
+# arithmetic: scores, exponentials and every sum in fp32; P rounded to the
+# input type before P V and P^T dO, dS before dS K and dS^T Q; D from the
+# stored O; O written in the input type, gradients in fp32.  Used where the
+# flat bar above does not scale: softmax scales far from 1/sqrt(d), whose
+# outputs and gradients grow with the scale.
+UNIT = {torch.float32: 2.0 ** -24, torch.float16: 2.0 ** -11, torch.bfloat16: 2.0 ** -8}
+SUBNORMAL = {torch.float32: 0.0, torch.float16: 2.0 ** -25, torch.bfloat16: 0.0}
+ACC = 2.0 ** -20          # fp32 sums of up to a few thousand terms, relative to sum |terms|
+
+
+def _p_rel(t, q, k, scale):
+    """Relative error of the kernel's P_ij = exp(s_ij - lse_i): fp32 score
+    and row statistic, each within a few ulp of its magnitude."""
+    lse = np.where(np.isfinite(t["lse"]), np.abs(t["lse"]), 0.0)
+    return 2.0 ** -21 * (scale * (np.abs(q) @ np.abs(k).T) + lse[:, None]) + 2.0 ** -22
+
+
+def forward_bound(t, q, k, v, scale, dtype):
+    """|o_kernel - o| per element: P's rounding (and its fp32 error) weighted
+    by |v|, the P V sum, and the output's own rounding."""
+    u, sub = UNIT[dtype], SUBNORMAL[dtype]
+    p, av = t["p"], np.abs(v)
+    w = (u + _p_rel(t, q, k, scale) + ACC) * p + sub * (p > 0)
+    return w @ av + u * np.abs(t["o"]) + 1e-6
+
+
+def backward_bound(t, q, k, v, do, o_in, scale, dtype):
+    """(dq, dk, dv) per-element bounds for a backward handed the output o_in
+    (the pages' backward reads O from memory and forms D_i = sum_c dO_ic O_ic
+    from it).  D then differs from the oracle's by the known
+    dD_i = sum_c dO_ic (o_in - o)_ic, which shifts dS_ij by -P_ij dD_i: that
+    shift enters dq and dk as the signed sums it is.  The rest is bounded
+    term by term: P's relative error, dP's and D's fp32 sums, dS's (and,
+    for dv, P's) rounding to the input type, each weighted by |k|, |q| or
+    |dO|."""
+    u, sub = UNIT[dtype], SUBNORMAL[dtype]
+    p, ds = t["p"], np.abs(t["ds"])
+    aq, ak, av, ado = np.abs(q), np.abs(k), np.abs(v), np.abs(do)
+    rho = _p_rel(t, q, k, scale)
+    o_in = np.asarray(o_in, dtype=np.float64)
+    dd = (np.asarray(do, dtype=np.float64) * (o_in - t["o"])).sum(axis=1)
+    acc = ACC * (ado @ av.T) + 2 * ACC * (ado * np.abs(o_in)).sum(axis=1)[:, None]
+    e_ds = (u + rho + ACC) * ds + (1 + u) * p * acc + u * p * np.abs(dd)[:, None] \
+        + sub * (p > 0)
+    e_dq = scale * (e_ds @ ak + np.abs(dd[:, None] * (p @ k)))
+    e_dk = scale * (e_ds.T @ aq + np.abs((p * dd[:, None]).T @ q))
+    e_dv = ((u + rho + ACC) * p + sub * (p > 0)).T @ ado
+    return e_dq + 1e-6, e_dk + 1e-6, e_dv + 1e-6
+
+
+def assert_within(name, got, ref, bound):
+    """Every element of got within its own bound of ref."""
+    got, ref = np.asarray(got, dtype=np.float64), np.asarray(ref, dtype=np.float64)
+    assert not np.isnan(got).any(), f"{name}: NaN in result"
+    excess = np.abs(got - ref) - bound
+    worst = np.unravel_index(int(np.argmax(excess)), excess.shape) if excess.size else None
+    assert excess.size == 0 or excess.max() <= 0, \
+        f"{name}: {np.abs(got - ref)[worst]:.3e} at {worst} over its bound {bound[worst]:.3e}"
+    return float(np.max(np.abs(got - ref) / bound, initial=0.0))

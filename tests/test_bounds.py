@@ -1,0 +1,60 @@
+"""The per-element rounding bounds of tests.parity (used by the GPU tests at
+softmax scales away from 1/sqrt(d)) must cover a float64 emulation of the
+kernels' rounding points: P rounded to the input type before P V and
+P^T dO, dS rounded before dS K and dS^T Q, D from the O handed to the
+backward, O rounded on output.  A bound that drops one of those terms fails
+here on the CPU.  The bounds must also stay useful: within a small multiple
+of the emulated error."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_io_aware_34_amd import workloads as W
+from tests.parity import DT, backward_bound, f64, forward_bound
+
+
+def rnd(x, dt):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dt).double().numpy()
+
+
+@pytest.mark.parametrize("N,d,dtype,causal,scale", [
+    (200, 64, "bf16", True, 1.0), (150, 128, "bf16", False, 0.3), (180, 64, "f16", True, 0.5),
+    (130, 64, "bf16", False, None)])
+def test_bounds_cover_rounding_emulation(N, d, dtype, causal, scale):
+    dt = DT[dtype]
+    sc = W.scale_for(d) if scale is None else scale
+    q, k, v, do = W.draw_qkvdo(1, 1, N, d, dtype, seed=N)
+    a = [f64(x[0, 0]) for x in (q, k, v, do)]
+    t = oracle.backward_head_terms(*a, sc, causal)
+    p = t["p"]
+    o_emul = rnd(rnd(p, dt) @ a[2], dt)
+    fb = forward_bound(t, *a[:3], sc, dt)
+    assert np.all(np.abs(o_emul - t["o"]) <= fb)
+    assert fb.max() <= 8 * np.abs(o_emul - t["o"]).max() + 1e-5
+    o_in = rnd(t["o"], dt)
+    d_row = (a[3] * o_in).sum(axis=1)
+    ds16 = rnd(p * (a[3] @ a[2].T - d_row[:, None]), dt)
+    emul = (sc * ds16 @ a[1], sc * ds16.T @ a[0], rnd(p, dt).T @ a[3])
+    g = oracle.backward_head(*a, sc, causal)
+    for name, e, ref, bnd in zip(("dq", "dk", "dv"), emul, g, backward_bound(t, *a, o_in, sc, dt)):
+        err = np.abs(e - ref)
+        assert np.all(err <= bnd), name
+        # useful: the bound is within 8x of the largest emulated error (1.1-5x measured)
+        assert bnd.max() <= 8 * err.max() + 1e-5, (name, bnd.max(), err.max())
+
+
+def test_bound_catches_a_dropped_rounding():
+    """Emulating dS rounded at a quarter of the precision (a rounding step
+    the bound does not allow for) must break the dq bound somewhere."""
+    N, d, sc, dt = 160, 64, 1.0, torch.bfloat16
+    q, k, v, do = W.draw_qkvdo(1, 1, N, d, "bf16", seed=5)
+    a = [f64(x[0, 0]) for x in (q, k, v, do)]
+    t = oracle.backward_head_terms(*a, sc, True)
+    o_in = rnd(t["o"], dt)
+    ds = t["p"] * (a[3] @ a[2].T - (a[3] * o_in).sum(axis=1)[:, None])
+    coarse = np.round(ds * 2.0 ** 5) / 2.0 ** 5          # absolute step 2^-5
+    dq = sc * coarse @ a[1]
+    g = oracle.backward_head(*a, sc, True)
+    assert np.any(np.abs(dq - g[0]) > backward_bound(t, *a, o_in, sc, dt)[0])

@@ -186,3 +186,29 @@ def test_sampled_gradients_finite_differences():
     fq, fk, fv = finite_difference_grads(q, k, v, do, 0.35, True, None, 4)
     for got, ref in ((dq, fq[rows]), (dk, fk[cols]), (dv, fv[cols])):
         assert np.max(np.abs(got - ref)) <= 1e-6 * max(1e-12, np.max(np.abs(ref)))
+
+
+@pytest.mark.parametrize("causal,masked", [(False, False), (True, True)])
+def test_backward_terms(causal, masked):
+    """backward_head_terms: P's rows sum to 1 (0 on a row with no allowed
+    key), dS's rows sum to 0 (sum_j P_ij (dP_ij - D_i) = D_i - D_i), and
+    scale dS K, scale dS^T Q, P^T dO, P V give backward_head's gradients and
+    forward_head's output."""
+    n, d, scale = 300, 16, 0.4
+    q, k, v, do = (randn(n, d) for _ in range(4))
+    bm = None
+    if masked:
+        bm = np.ones((3, 3), dtype=np.uint8)
+        bm[1, :] = 0
+    t = oracle.backward_head_terms(q, k, v, do, scale, causal, bm, mask_block=128)
+    live = np.ones(n, dtype=bool) if bm is None else (np.arange(n) // 128) != 1
+    np.testing.assert_allclose(t["p"].sum(axis=1), live.astype(float), atol=1e-12)
+    np.testing.assert_allclose(t["ds"].sum(axis=1), 0.0, atol=1e-12)
+    assert np.all(np.isneginf(t["lse"][~live]))
+    o, lse = forward_head(q, k, v, scale, causal, bm)
+    np.testing.assert_allclose(t["o"], o, atol=1e-12)
+    np.testing.assert_allclose(t["lse"], lse, atol=1e-12)
+    dq, dk, dv = backward_head(q, k, v, do, scale, causal, bm)
+    np.testing.assert_allclose(scale * t["ds"] @ k, dq, atol=1e-12)
+    np.testing.assert_allclose(scale * t["ds"].T @ q, dk, atol=1e-12)
+    np.testing.assert_allclose(t["p"].T @ do, dv, atol=1e-12)
