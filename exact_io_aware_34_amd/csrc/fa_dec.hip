@@ -272,9 +272,13 @@ __global__ __launch_bounds__(256, dec_waves(D)) void dec_kernel(DecParams p) {
 }
 
 // Merge of the key ranges: one thread per (row, column), D threads per row.
+// The ranges are read in groups of MG, every load of a group issued before
+// any is used, so a row costs two memory round trips per group (one for the
+// max of the range statistics, one for the weighted sum) rather than two
+// per range.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void dec_combine_kernel(DecParams p) {
-  constexpr int RPB = 256 / D;
+  constexpr int RPB = 256 / D, MG = 8;
   const int row = blockIdx.x * RPB + threadIdx.x / D, d = threadIdx.x % D;
   const int rows = p.BH * p.Nq;
   if (row >= rows) return;
@@ -282,16 +286,32 @@ __global__ __launch_bounds__(256) void dec_combine_kernel(DecParams p) {
   const int bh = row / Nq, q = row - bh * Nq;
   const size_t r0 = (size_t)bh * S * Nq + q;   // partial row of range 0; stride Nq
   float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, p.lse_part[r0 + (size_t)s * Nq]);
+  for (int s0 = 0; s0 < S; s0 += MG) {
+    float lv[MG];
+#pragma unroll
+    for (int j = 0; j < MG; ++j)
+      lv[j] = s0 + j < S ? p.lse_part[r0 + (size_t)(s0 + j) * Nq] : -INFINITY;
+#pragma unroll
+    for (int j = 0; j < MG; ++j) M = fmaxf(M, lv[j]);
+  }
   float ov = 0.f, lse = -INFINITY;
   if (M != -INFINITY) {
     constexpr float kLog2e = 1.4426950408889634f;
     float W = 0.f, acc = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const size_t r = r0 + (size_t)s * Nq;
-      const float wt = fast_exp2((p.lse_part[r] - M) * kLog2e);
-      W += wt;
-      acc = fmaf(wt, p.o_part[r * D + d], acc);
+    for (int s0 = 0; s0 < S; s0 += MG) {
+      float lv[MG], xv[MG];
+#pragma unroll
+      for (int j = 0; j < MG; ++j) {
+        const size_t r = r0 + (size_t)(s0 + j) * Nq;
+        lv[j] = s0 + j < S ? p.lse_part[r] : -INFINITY;
+        xv[j] = s0 + j < S ? p.o_part[r * D + d] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < MG; ++j) {
+        const float wt = fast_exp2((lv[j] - M) * kLog2e);
+        W += wt;
+        acc = fmaf(wt, xv[j], acc);
+      }
     }
     ov = acc / W;
     lse = M + __logf(W);
