@@ -14,6 +14,7 @@ library has not been built (there is no other code path).
 """
 
 import ctypes
+import functools
 import os
 
 import torch  # loads torch's HIP runtime first, so libfa.so binds to the same one
@@ -142,6 +143,7 @@ def _mask_arg(block_mask, n):
     return block_mask
 
 
+@functools.lru_cache(maxsize=256)
 def default_scale(d: int) -> float:
     return float(torch.tensor(d ** -0.5, dtype=torch.float32))
 
@@ -152,6 +154,7 @@ def _dtype_code(dtype):
     return DTYPE_CODES[dtype]
 
 
+@functools.lru_cache(maxsize=256)
 def forward_splits(B, H, N, d, n_splits=0, dtype=torch.bfloat16) -> int:
     """Number of key runs fa_forward_split uses for this shape and input dtype
     (0 on bad input)."""
@@ -163,6 +166,7 @@ def fa_forward_splits_used(B, H, N, d, n_splits, dtype=torch.bfloat16) -> int:
     return forward_splits(B, H, N, d, n_splits, dtype) if n_splits != 1 else 1
 
 
+@functools.lru_cache(maxsize=256)
 def forward_split_workspace_size(B, H, N, d, n_splits=0, dtype=torch.bfloat16) -> int:
     return int(_lib.fa_forward_split_workspace_size(B, H, N, d, n_splits, _dtype_code(dtype)))
 
@@ -213,6 +217,7 @@ def forward(q, k, v, causal=False, scale=None, block_mask=None, out=None, lse=No
     return o, lse
 
 
+@functools.lru_cache(maxsize=256)
 def workspace_size(B, H, N, d) -> int:
     return int(_lib.fa_backward_workspace_size(B, H, N, d))
 
@@ -261,11 +266,13 @@ def backward(q, k, v, o, lse, do, causal=False, scale=None, block_mask=None,
     return dq, dk, dv
 
 
+@functools.lru_cache(maxsize=256)
 def decode_splits(B, H, Nq, Nk, d, n_splits=0) -> int:
     """Number of key ranges fa_decode uses for this shape (0 on bad input)."""
     return int(_lib.fa_decode_splits(B, H, Nq, Nk, d, n_splits))
 
 
+@functools.lru_cache(maxsize=256)
 def decode_workspace_size(B, H, Nq, Nk, d, n_splits=0) -> int:
     return int(_lib.fa_decode_workspace_size(B, H, Nq, Nk, d, n_splits))
 
@@ -333,6 +340,7 @@ def decode_noalloc(q, k, v, causal=False, scale=None, n_splits=0, out=None, lse=
     return o, lse
 
 
+@functools.lru_cache(maxsize=256)
 def fp8_workspace_size(B, H, N, d) -> int:
     return int(_lib.fa_forward_fp8_workspace_size(B, H, N, d))
 
