@@ -38,7 +38,9 @@ fa_forward_split with the library's number of key runs.
 
 The FP8 forward (fa_forward_fp8: rotation + block quantisation, then
 attention on E4M3 operands) is timed on the same workload and reported in the
-`fp8` object: call time (both kernels) and the preparation alone, the
+`fp8` object: call time (both kernels), fa_fp8_prepare of all three
+operands alone (the forward prepares K and V that way and each query
+tile's Q inside its attention kernel), the
 workload's forward FLOPs (same count as the 16-bit forward) over the call
 time against the 5.0 PFLOP/s dense FP8 peak, and the oracle's float64
 emulation of the method on a sample of heads.

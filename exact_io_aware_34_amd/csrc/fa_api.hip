@@ -124,6 +124,7 @@ int fp8_setup(fa::Fp8Params& p, const void* q, const void* k, const void* v, int
               int d, float scale, int dtype, const int8_t* signs, void* workspace,
               size_t workspace_bytes) {
   if (!tensor_ptr_ok(q) || !tensor_ptr_ok(k) || !tensor_ptr_ok(v)) return FA_ERR_INVALID_ARG;
+  if (signs != nullptr && !aligned(signs, 16)) return FA_ERR_INVALID_ARG;
   const int rc = check_common(B, H, N, d, scale, dtype);
   if (rc != FA_OK) return rc;
   if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
@@ -155,7 +156,7 @@ int fp8_setup(fa::Fp8Params& p, const void* q, const void* k, const void* v, int
 
 extern "C" {
 
-int fa_abi_version(void) { return 4; }
+int fa_abi_version(void) { return 5; }
 
 const char* fa_status_string(int status) {
   switch (status) {
@@ -449,6 +450,7 @@ int fa_forward_fp8(const void* q, const void* k, const void* v, void* o, float* 
   p.o = o;
   p.lse = lse;
   p.mask = block_mask;
+  p.prep_z0 = 1;   // K and V; each query tile's Q is prepared by the attention kernel
   const hipError_t e = fa::launch_fp8(p, dtype, d, causal != 0, true, true, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

@@ -26,7 +26,9 @@
 //     K8 are written row-major (rows padded to a multiple of 64 with zeros);
 //     V8 is written transposed per 64-key block, [d][64], with the keys of a
 //     block permuted so that each lane's slice of a row is exactly the 32
-//     keys it multiplies in the P V product.
+//     keys it multiplies in the P V product.  The forward runs it on K and
+//     V only: fwd8_kernel prepares each query tile's Q itself, with the same
+//     arithmetic (and so the same codes).
 //   * fwd8_kernel: the 16-bit forward's grid and causal / block-sparse tile
 //     skipping, 64-key K and V^T tiles in a three-slot LDS ring filled by
 //     direct global->LDS copies, S^T = K Q^T and O^T += V^T P^T on
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8Params p) {
   __shared__ __attribute__((aligned(16))) uint8_t vtile[64 * RSB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int z = blockIdx.y;         // 0 = Q, 1 = K, 2 = V
+  const int z = blockIdx.y + p.prep_z0;   // 0 = Q, 1 = K, 2 = V
   const int nt = p.n_t64;
   const int bh = blockIdx.x / nt, t = blockIdx.x - bh * nt;
   const int row = tid >> 2, qd = tid & 3;
@@ -235,6 +237,7 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8Params p) {
 template <typename T, int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
   using HT = typename V8<T>::h;
+  using VT = typename V8<T>::t;
   constexpr int NW = 4, BR = 128, BC = 64, NS = 3;
   constexpr int TB = BC * D;                 // bytes of a K tile (and of a V^T tile)
   constexpr int DH = D / 64;                 // score MFMAs per 32-key unit
@@ -247,6 +250,7 @@ __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
   // Block scales of the tile in each slot: [0] its K scale, [1] its V scale
   // (lanes 2.. of the copy repeat them).
   __shared__ __attribute__((aligned(16))) float sc_s[NS][64];
+  __shared__ float qam_s[NW];   // Q amax of each wave's 32 rows
   __shared__ uint8_t mask_s[SPARSE ? FWD_MAX_MASK_TILES : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -332,23 +336,127 @@ __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
     dma4((lane & 1) ? svh + jj : skh + jj, lds_addr(&sc_s[slot][0]));
   };
 
+
+  // Q^T (B operand): lane holds query q = q0w + l32, elements 64 h + 32 g
+  // .. + 31 of c Q R, rotated and quantised here from the 16-bit rows with
+  // the preparation kernel's arithmetic: the same sign flips, butterflies in
+  // the same order of element-index bits (0-4 in the lane, 5 across the two
+  // lane halves, 6 across h), the same factors and block scale (the 64-row
+  // block is this wave and its neighbour), so the codes are the ones
+  // fa_fp8_prepare writes for Q.
+  // The rows are loaded before the first tile copies are issued, so that
+  // waiting for them leaves the copies in flight.
+  i32x8 qf[DH];
+  int eq;
+  VT qraw[DH][4];
+  i32x8 sgn[DH];
+  {
+    const int q = q0w + l32;
+    const T* qr = (const T*)p.q + ((size_t)bh * N + min(q, N - 1)) * D + 32 * g;
+#pragma unroll
+    for (int h = 0; h < DH; ++h)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qraw[h][c] = *(const VT*)(qr + 64 * h + 8 * c);
+    if (p.signs != nullptr) {
+#pragma unroll
+      for (int h = 0; h < DH; ++h) sgn[h] = *(const i32x8*)(p.signs + 64 * h + 32 * g);
+    }
+  }
   int jq[NS];
   jq[0] = next_active(0);
   jq[1] = jq[0] < kt_end ? next_active(jq[0] + 1) : kt_end;
   jq[2] = jq[1] < kt_end ? next_active(jq[1] + 1) : kt_end;
   if (jq[0] < kt_end) issue(jq[0], 0);
   if (jq[1] < kt_end) issue(jq[1], 1);
-
-  // Q^T (B operand): lane holds query q0w + l32, bytes 64 h + 32 g .. + 31.
-  i32x8 qf[DH];
   {
-    const int q = q0w + l32;
+    const bool live = q0w + l32 < N;
+    float x[DH][32];
 #pragma unroll
     for (int h = 0; h < DH; ++h)
-      qf[h] = q < N ? *(const i32x8*)(p.q8 + ((size_t)bh * p.Npad + q) * D + 64 * h + 32 * g)
-                    : i32x8{};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        // Packed pairs (elements 8c + 2i, 8c + 2i + 1); rows past N are zero.
+        u32x4 w = __builtin_bit_cast(u32x4, qraw[h][c]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t pr = live ? w[i] : 0u;
+          if (p.signs != nullptr) {
+            // Sign bytes of the pair (bytes 2(i%2), 2(i%2)+1 of dword (8c+2i)/4)
+            // onto the pair's two sign bits: an exact negation.
+            const uint32_t sw = (uint32_t)sgn[h][2 * c + i / 2];
+            const uint32_t m = __builtin_amdgcn_perm(0u, sw, (i & 1) ? 0x030c020cu : 0x010c000cu);
+            pr ^= m & 0x80008000u;
+          }
+          const uint16_t lo = (uint16_t)pr, hi = (uint16_t)(pr >> 16);
+          x[h][8 * c + 2 * i] = (float)__builtin_bit_cast(T, lo);
+          x[h][8 * c + 2 * i + 1] = (float)__builtin_bit_cast(T, hi);
+        }
+      }
+    if (p.signs != nullptr) {
+#pragma unroll
+      for (int hs = 1; hs < 32; hs *= 2)
+#pragma unroll
+        for (int h = 0; h < DH; ++h)
+#pragma unroll
+          for (int i = 0; i < 32; ++i)
+            if ((i & hs) == 0) {
+              const float a = x[h][i], b = x[h][i + hs];
+              x[h][i] = a + b;
+              x[h][i + hs] = a - b;
+            }
+      // Element-index bit 5 is the lane half: the swap hands every lane the
+      // low half's value (a) and the high half's (b) of its pair.
+#pragma unroll
+      for (int h = 0; h < DH; ++h)
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+          const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[h][e]),
+                                                          __float_as_uint(x[h][e]), false, false);
+          const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+          x[h][e] = g ? a - b : a + b;
+        }
+      if constexpr (DH == 2) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+          const float a = x[0][e], b = x[1][e];
+          x[0][e] = a + b;
+          x[1][e] = a - b;
+        }
+      }
+      const float rs = p.rsqrt_d * p.scale_log2e;
+#pragma unroll
+      for (int h = 0; h < DH; ++h)
+#pragma unroll
+        for (int e = 0; e < 32; ++e) x[h][e] *= rs;
+    } else {
+#pragma unroll
+      for (int h = 0; h < DH; ++h)
+#pragma unroll
+        for (int e = 0; e < 32; ++e) x[h][e] *= p.scale_log2e;
+    }
+    float am = 0.f;
+#pragma unroll
+    for (int h = 0; h < DH; ++h)
+#pragma unroll
+      for (int e = 0; e < 32; ++e) am = fmaxf(am, fabsf(x[h][e]));
+    am = wave_max(am);
+    if (lane == 0) qam_s[wave] = am;
+    lds_reads_done();   // the write above has completed
+    wg_barrier();
+    am = fmaxf(qam_s[wave & 2], qam_s[(wave & 2) | 1]);
+    const float bs = pow2_block_scale(am);
+    const float inv = __uint_as_float((uint32_t)(254 - e8m0_of(bs)) << 23);   // 1 / bs, exact
+    eq = e8m0_of(bs);
+#pragma unroll
+    for (int h = 0; h < DH; ++h)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = fminf(fmaxf(x[h][4 * i + e] * inv, -kE4M3Max), kE4M3Max);
+        qf[h][i] = pack_e4m3(y[0], y[1], y[2], y[3]);
+      }
   }
-  const int eq = e8m0_of(p.sq[(size_t)bh * nt + min(q0w, N - 1) / 64]);
   wait_all_loads();
 
   f32x16 o[DB];
@@ -488,8 +596,8 @@ template <typename T, int D>
 hipError_t launch_fp8_t(const Fp8Params& p, bool causal, bool sparse, bool prep, bool attend,
                         hipStream_t st) {
   if (prep) {
-    hipLaunchKernelGGL((fp8_prep_kernel<T, D>), dim3((unsigned)(p.BH * p.n_t64), 3), dim3(256), 0,
-                       st, p);
+    hipLaunchKernelGGL((fp8_prep_kernel<T, D>), dim3((unsigned)(p.BH * p.n_t64), 3 - p.prep_z0),
+                       dim3(256), 0, st, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || !attend) return e;
   }

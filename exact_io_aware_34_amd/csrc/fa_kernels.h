@@ -157,6 +157,8 @@ struct Fp8Params {
   const uint8_t* mask;  // nullptr = dense
   int BH, N, Npad, n_t64, mask_tiles;
   float scale_log2e, rsqrt_d;
+  // Preparation: operands prep_z0 .. 2 (0 = Q, 1 = K, 2 = V), one grid row each.
+  int prep_z0;
 };
 
 struct DropMaskParams {

@@ -351,6 +351,8 @@ def _fp8_args(q, k, v, signs, workspace):
     if signs is not None:
         if signs.dtype != torch.int8 or tuple(signs.shape) != (d,) or not signs.is_cuda:
             raise ValueError(f"signs must be an int8 GPU tensor of shape ({d},)")
+        if not signs.is_contiguous() or signs.data_ptr() % 16:
+            raise ValueError("signs must be contiguous and 16-byte aligned")
     ws_bytes = fp8_workspace_size(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)

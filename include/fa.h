@@ -283,13 +283,18 @@ int fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, floa
  * of |O| on N(0, 1) inputs); it is not exact.
  *
  * q, k, v: (B,H,N,d) FA_BF16 or FA_F16; o: same shape and dtype; lse: (B,H,N)
- * fp32.  `signs`: device pointer to d int8 values (negative = -1, otherwise
- * +1), the random signs of the rotation, drawn by the caller; NULL skips the
- * rotation (block-quantised FP8 without incoherent processing).  causal and
+ * fp32.  `signs`: device pointer (16-byte aligned) to d int8 values
+ * (negative = -1, otherwise +1), the random signs of the rotation, drawn by
+ * the caller; NULL skips the rotation (block-quantised FP8 without incoherent
+ * processing).  causal and
  * block_mask as for fa_forward.  `workspace` (at least
  * fa_forward_fp8_workspace_size() bytes, 256-byte aligned, caller-owned)
- * receives the prepared operands, in this order, each region padded to 256
- * bytes, with nt = ceil(N / 64) and Npad = 64 nt:
+ * holds the prepared operands, in this order, each region padded to 256
+ * bytes, with nt = ceil(N / 64) and Npad = 64 nt (fa_forward_fp8 writes the
+ * K and V regions; each query tile's c Q R is rotated and quantised inside
+ * the attention kernel, with the same arithmetic and so the same codes and
+ * scales fa_fp8_prepare writes to the Q regions, which fa_forward_fp8
+ * leaves untouched):
  *   Q8  (B*H, Npad, d) E4M3 codes, row-major (rows >= N are zero)
  *   K8  (B*H, Npad, d) E4M3 codes
  *   V8T (B*H, nt, d, 64) E4M3 codes of each 64-key block transposed, position
@@ -317,10 +322,12 @@ size_t fa_forward_fp8_workspace_size(int B, int H, int N, int d);
 /* Static, human-readable text for a status code. */
 const char* fa_status_string(int status);
 
-/* Library ABI version (this header: 4; 2 added fa_forward_split*, 3 the fp32
+/* Library ABI version (this header: 5; 2 added fa_forward_split*, 3 the fp32
  * output o_acc of the dropout calls, 4 power-of-two FP8 block scales, the
  * scale argument of fa_fp8_prepare and the dtype argument of
- * fa_forward_splits and fa_forward_split_workspace_size). */
+ * fa_forward_splits and fa_forward_split_workspace_size, 5 fa_forward_fp8
+ * no longer writing the Q regions of its workspace, and `signs` 16-byte
+ * aligned). */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

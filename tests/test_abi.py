@@ -68,7 +68,7 @@ def test_header_declares_the_boundary():
 def test_every_declared_symbol_is_exported(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.fa_abi_version() == 4
+    assert lib.fa_abi_version() == 5
 
 
 def test_status_strings(lib):
@@ -237,6 +237,11 @@ def test_fp8_validation(lib):
                               None) == -1                      # scale must be finite and > 0
     assert lib.fa_fp8_prepare(FAKE, FAKE, FAKE, 2, 3, 100, 64, float("nan"), 2, None, FAKE, need,
                               None) == -1
+    # the rotation signs are read as 16-byte vectors
+    assert lib.fa_fp8_prepare(FAKE, FAKE, FAKE, 2, 3, 100, 64, 0.125, 2, MISALIGNED, FAKE, need,
+                              None) == -1
+    assert lib.fa_forward_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 3, 100, 64, 0.125, 1, None, 2,
+                              ctypes.c_void_p((1 << 20) + 8), FAKE, need, None) == -1
 
 
 def test_dropout_validation(lib):
