@@ -54,6 +54,9 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kE4M3Max = 448.f;
 
+template <int V>
+using ic = std::integral_constant<int, V>;
+
 // c + (2^(ea-127) A)(2^(eb-127) B): formats 0/0, both operands E4M3; ea and eb
 // are E8M0 exponents (byte 0 of the scale operands), the same for every lane.
 __device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c, int ea, int eb) {
@@ -325,7 +328,8 @@ __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
   // (rows past N are zero in both tiles: the preparation pads them).  The
   // scales travel with the tiles, so the wait that makes a tile visible
   // covers them too.
-  auto issue = [&](int jj, int slot) {
+  auto issue = [&](int jj, auto slc) __attribute__((always_inline)) {
+    constexpr int slot = decltype(slc)::value;
     const uint8_t* ks = K8 + (size_t)jj * TB;
     const uint8_t* vs = V8 + (size_t)jj * TB;
     const uint32_t kd = lds0 + (uint32_t)(slot * TB), vd = lds0 + (uint32_t)((NS + slot) * TB);
@@ -366,8 +370,8 @@ __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
   jq[0] = next_active(0);
   jq[1] = jq[0] < kt_end ? next_active(jq[0] + 1) : kt_end;
   jq[2] = jq[1] < kt_end ? next_active(jq[1] + 1) : kt_end;
-  if (jq[0] < kt_end) issue(jq[0], 0);
-  if (jq[1] < kt_end) issue(jq[1], 1);
+  if (jq[0] < kt_end) issue(jq[0], ic<0>{});
+  if (jq[1] < kt_end) issue(jq[1], ic<1>{});
   {
     const bool live = q0w + l32 < N;
     float x[DH][32];
@@ -472,13 +476,16 @@ __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
   // rebuilding the splat before every tile.
   asm volatile("" : "+v"(negm));
 
-  int slot = 0;
-  while (jq[0] < kt_end) {
+  // One tile; the ring slot is a compile-time constant (the loop below is
+  // unrolled over the three slots), so every LDS address folds into an
+  // instruction's offset.
+  auto iter = [&](auto slc) __attribute__((always_inline)) {
+    constexpr int slot = decltype(slc)::value;
     const int j = jq[0];
     if (jq[1] < kt_end) wait_vmcnt<OPS>();
     else wait_vmcnt<0>();
     wg_barrier();
-    if (jq[2] < kt_end) issue(jq[2], slot == 0 ? 2 : slot - 1);
+    if (jq[2] < kt_end) issue(jq[2], ic<(slot + NS - 1) % NS>{});
     if (j * BC <= last_key) {
       const uint8_t* kt = kvs + slot * TB;
       const uint8_t* vt = kvs + slot * TB;   // V^T offsets already include NS * TB
@@ -569,7 +576,14 @@ __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
     jq[0] = jq[1];
     jq[1] = jq[2];
     jq[2] = jq[1] < kt_end ? next_active(jq[1] + 1) : kt_end;
-    slot = slot == NS - 1 ? 0 : slot + 1;
+  };
+  static_assert(NS == 3, "the loop below unrolls three slots");
+  while (jq[0] < kt_end) {
+    iter(ic<0>{});
+    if (jq[0] >= kt_end) break;
+    iter(ic<1>{});
+    if (jq[0] >= kt_end) break;
+    iter(ic<2>{});
   }
 
   // Epilogue: O = O / l, lse = (m + log2 l) * ln 2.
