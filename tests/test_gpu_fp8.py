@@ -370,3 +370,29 @@ def test_fp8_full_size_sampled(fa, name, heads, rows):
         assert err_k <= 1.25 * err_e + 2e-4
         assert dist <= 0.75 * err_e + 2e-4
         assert lse_x <= 0, f"[{b},{h}] lse over its bound by {lse_x:.3e}"
+
+
+def test_fp8_forward_workspace_contract(fa):
+    """fa_forward_fp8 writes the K and V regions of its workspace (the same
+    codes and scales fa_fp8_prepare writes) and leaves the Q regions alone;
+    misaligned rotation signs are refused before any launch."""
+    B, H, N, d = 1, 2, 300, 64
+    q, k, v, _ = W.draw_qkvdo(B, H, N, d, "bf16", seed=31)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    signs = W.draw_rotation_signs(d, seed=2).cuda()
+    size = fa.fp8_workspace_size(B, H, N, d)
+    ws_f = torch.full((size,), 0xA5, dtype=torch.uint8, device="cuda")
+    ws_p = torch.zeros(size, dtype=torch.uint8, device="cuda")
+    fa.forward_fp8(qd, kd, vd, signs=signs, causal=True, workspace=ws_f)
+    fa.fp8_prepare(qd, kd, vd, signs, workspace=ws_p)
+    torch.cuda.synchronize()
+    (q8f, k8f, v8f), (sqf, skf, svf) = fa.fp8_views(ws_f, B, H, N, d)
+    (_, k8p, v8p), (_, skp, svp) = fa.fp8_views(ws_p, B, H, N, d)
+    assert torch.all(q8f == 0xA5)
+    assert torch.all(sqf.view(torch.uint8) == 0xA5)
+    assert torch.equal(k8f, k8p) and torch.equal(v8f, v8p)
+    assert torch.equal(skf, skp) and torch.equal(svf, svp)
+    raw = torch.empty(d + 16, dtype=torch.int8, device="cuda")
+    raw[1:d + 1] = signs
+    with pytest.raises(ValueError):
+        fa.forward_fp8(qd, kd, vd, signs=raw[1:d + 1], causal=True)
