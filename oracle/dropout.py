@@ -97,14 +97,16 @@ def keep_mask(bh, rows, cols, seed, offset, p):
     return byte >= np.uint64(keep_threshold(p))
 
 
-def forward_head_dropout(q, k, v, scale, p, seed, offset, bh, causal=False, block_mask=None):
-    """(o, lse) of one head with dropout on the probabilities."""
+def forward_head_dropout(q, k, v, scale, p, seed, offset, bh, causal=False, block_mask=None,
+                         rows=None):
+    """(o, lse) of one head with dropout on the probabilities, at query rows
+    `rows` (default all): each row needs only its own scores and keep bytes."""
     q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
-    n = q.shape[0]
-    rows = np.arange(n)
-    s = scale * (q @ k.T)
+    n = k.shape[0]
+    rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    s = scale * (q[rows] @ k.T)
     pm, lse = _row_softmax(s, allowed(rows, n, causal, block_mask))
-    z = keep_mask(bh, rows, rows, seed, offset, p)
+    z = keep_mask(bh, rows, np.arange(n), seed, offset, p)
     return (pm * z) @ v * keep_scale(p), lse
 
 
@@ -128,3 +130,20 @@ def backward_head_dropout(q, k, v, do, scale, p, seed, offset, bh, causal=False,
     dp = (do @ v.T) * zc
     ds = pm * (dp - d[:, None])
     return scale * ds @ k, scale * ds.T @ q, pd.T @ do
+
+
+def dq_rows_dropout(q, k, v, do, scale, p, seed, offset, bh, rows, causal=False,
+                    block_mask=None):
+    """dq of one head with dropout at query rows `rows` only, by the same
+    definitions as backward_head_dropout: dq_i = scale sum_j dS_ij k_j needs
+    row i's P, keep bytes, dP and D_i = sum_c dO_ic O_ic alone."""
+    q, k, v, do = (np.asarray(t, dtype=np.float64) for t in (q, k, v, do))
+    n = k.shape[0]
+    rows = np.asarray(rows, dtype=np.int64)
+    s = scale * (q[rows] @ k.T)
+    pm, _ = _row_softmax(s, allowed(rows, n, causal, block_mask))
+    zc = keep_mask(bh, rows, np.arange(n), seed, offset, p) * keep_scale(p)
+    o = (pm * zc) @ v
+    d = np.sum(do[rows] * o, axis=1)
+    ds = pm * ((do[rows] @ v.T) * zc - d[:, None])
+    return scale * ds @ k

@@ -158,3 +158,45 @@ def test_dropout_changes_with_seed_and_offset(fa):
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[3])                  # deterministic
     assert not torch.equal(outs[0], outs[1]) and not torch.equal(outs[0], outs[2])
+
+
+FULL_SIZE = [
+    # workload, sampled (b, h), sampled rows
+    ("causal_b4h12_n8192_d64_bf16", [(0, 0), (3, 11), (1, 6)],
+     [0, 1, 3, 4, 127, 128, 4095, 5000, 8191]),
+    ("causal_b1h12_n23400_d64_f16", [(0, 0), (0, 11)], [0, 5, 128, 11701, 23399]),
+    ("sparse_b2h16_n16384_d128_bf16", [(0, 0), (1, 15)], [0, 129, 7777, 16383]),
+]
+
+
+@pytest.mark.parametrize("name,heads,rows", FULL_SIZE)
+def test_dropout_full_size_sampled(fa, name, heads, rows):
+    """The full-size workloads with fused dropout (p = 0.1, as the benchmark
+    runs them), forward then backward in the launch configuration the
+    benchmark times: O, lse and dQ at sampled rows of sampled heads against
+    the oracle (each of those needs only its own row of scores and keep
+    bytes), at the plain path's bound.  dK and dV need every row's D, so the
+    whole N x N keep mask: they are checked at the smaller sizes above."""
+    inp = W.make(name)
+    w = inp["workload"]
+    p, seed, offset = 0.1, 20260101, 0
+    qd, kd, vd, dod = (inp[n].cuda() for n in ("q", "k", "v", "do"))
+    md = None if inp["mask"] is None else inp["mask"].cuda()
+    o_acc = torch.empty(qd.shape, dtype=torch.float32, device="cuda")
+    o, lse = fa.forward(qd, kd, vd, causal=w.causal, scale=w.scale, block_mask=md, dropout_p=p,
+                        seed=seed, offset=offset, o_acc=o_acc)
+    dq, _, _ = fa.backward(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale,
+                           block_mask=md, dropout_p=p, seed=seed, offset=offset, o_acc=o_acc)
+    torch.cuda.synchronize()
+    rows = np.array(rows)
+    tol = TOL[inp["q"].dtype]
+    mnp = None if inp["mask"] is None else inp["mask"].numpy()
+    for b, h in heads:
+        a = [f64(inp[n][b, h]) for n in ("q", "k", "v", "do")]
+        bh = b * w.H + h
+        ro, rl = oracle.forward_head_dropout(a[0], a[1], a[2], w.scale, p, seed, offset, bh,
+                                             w.causal, mnp, rows=rows)
+        rq = oracle.dq_rows_dropout(*a, w.scale, p, seed, offset, bh, rows, w.causal, mnp)
+        assert_close(f"o[{b},{h}] rows", f64(o[b, h])[rows], ro, tol)
+        assert_close(f"lse[{b},{h}] rows", f64(lse[b, h])[rows], rl, LSE_TOL)
+        assert_close(f"dq[{b},{h}] rows", f64(dq[b, h])[rows], rq, tol)

@@ -275,3 +275,20 @@ def test_pins_catch_planted_slips():
     key, c = (1, 2), (0, 0, 0, 0)
     x = DR.philox(add_counter(c, 1), key, width=64)
     assert (x[1], x[0], x[3], x[2]) != numpy_philox_blocks(key, c, 1)[0]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_rows_match_the_whole_head(causal):
+    """forward_head_dropout(rows=...) and dq_rows_dropout give the whole-head
+    functions' values at those rows (each row needs only its own scores and
+    keep bytes), at rows on both sides of 4-row Philox blocks."""
+    n, d, p, seed, bh = 70, 8, 0.3, 987654321, 5
+    q, k, v, do = (RNG.standard_normal((n, d)) for _ in range(4))
+    rows = np.array([0, 3, 4, 33, 68, 69])
+    o, lse = DR.forward_head_dropout(q, k, v, 0.4, p, seed, 2, bh, causal)
+    o_r, lse_r = DR.forward_head_dropout(q, k, v, 0.4, p, seed, 2, bh, causal, rows=rows)
+    np.testing.assert_allclose(o_r, o[rows], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse_r, lse[rows], rtol=0, atol=1e-13)
+    dq, _, _ = DR.backward_head_dropout(q, k, v, do, 0.4, p, seed, 2, bh, causal)
+    dq_r = DR.dq_rows_dropout(q, k, v, do, 0.4, p, seed, 2, bh, rows, causal)
+    np.testing.assert_allclose(dq_r, dq[rows], rtol=0, atol=1e-12)
