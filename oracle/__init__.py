@@ -56,6 +56,7 @@ from .decode import (  # noqa: F401
 )
 from .dropout import (  # noqa: F401
     backward_head_dropout,
+    backward_head_dropout_terms,
     dq_rows_dropout,
     forward_head_dropout,
     keep_mask,

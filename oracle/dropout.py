@@ -147,3 +147,21 @@ def dq_rows_dropout(q, k, v, do, scale, p, seed, offset, bh, rows, causal=False,
     d = np.sum(do[rows] * o, axis=1)
     ds = pm * ((do[rows] @ v.T) * zc - d[:, None])
     return scale * ds @ k
+
+
+def backward_head_dropout_terms(q, k, v, do, scale, p, seed, offset, bh, causal=False,
+                                block_mask=None):
+    """One head's intermediate quantities of backward_head_dropout, whole
+    (N x N): {"p": P, "zc": Z / (1 - p), "ds": dS, "lse": lse, "o": O} with
+    O = (P o Z) V / (1 - p), by the same definitions.  Tests bound a kernel's
+    rounding error with them; small N only."""
+    q, k, v, do = (np.asarray(t, dtype=np.float64) for t in (q, k, v, do))
+    n = q.shape[0]
+    rows = np.arange(n)
+    s = scale * (q @ k.T)
+    pm, lse = _row_softmax(s, allowed(rows, n, causal, block_mask))
+    zc = keep_mask(bh, rows, rows, seed, offset, p) * keep_scale(p)
+    o = (pm * zc) @ v
+    d = np.sum(do * o, axis=1)
+    ds = pm * ((do @ v.T) * zc - d[:, None])
+    return {"p": pm, "zc": zc, "ds": ds, "lse": lse, "o": o}

@@ -127,13 +127,15 @@ def _p_rel(t, q, k, scale):
     return 2.0 ** -21 * (scale * (np.abs(q) @ np.abs(k).T) + lse[:, None]) + 2.0 ** -22
 
 
-def forward_bound(t, q, k, v, scale, dtype):
+def forward_bound(t, q, k, v, scale, dtype, out_rounded=True):
     """|o_kernel - o| per element: P's rounding (and its fp32 error) weighted
-    by |v|, the P V sum, and the output's own rounding."""
+    by |v|, the P V sum, and the output's own rounding (out_rounded=False for
+    the fp32 output of the dropout forward).  With dropout, t["zc"] (the keep
+    mask times 1 / (1 - p)) weights each P in the P V product."""
     u, sub = UNIT[dtype], SUBNORMAL[dtype]
-    p, av = t["p"], np.abs(v)
+    p, av = t["p"] * t.get("zc", 1.0), np.abs(v)
     w = (u + _p_rel(t, q, k, scale) + ACC) * p + sub * (p > 0)
-    return w @ av + u * np.abs(t["o"]) + 1e-6
+    return w @ av + (u if out_rounded else ACC) * np.abs(t["o"]) + 1e-6
 
 
 def backward_bound(t, q, k, v, do, o_in, scale, dtype):
@@ -147,16 +149,18 @@ def backward_bound(t, q, k, v, do, o_in, scale, dtype):
     |dO|."""
     u, sub = UNIT[dtype], SUBNORMAL[dtype]
     p, ds = t["p"], np.abs(t["ds"])
+    zc = t.get("zc", 1.0)              # dropout: keep mask / (1 - p) on P in dV and on dP
     aq, ak, av, ado = np.abs(q), np.abs(k), np.abs(v), np.abs(do)
     rho = _p_rel(t, q, k, scale)
     o_in = np.asarray(o_in, dtype=np.float64)
     dd = (np.asarray(do, dtype=np.float64) * (o_in - t["o"])).sum(axis=1)
-    acc = ACC * (ado @ av.T) + 2 * ACC * (ado * np.abs(o_in)).sum(axis=1)[:, None]
+    acc = ACC * (ado @ av.T) * zc + 2 * ACC * (ado * np.abs(o_in)).sum(axis=1)[:, None]
     e_ds = (u + rho + ACC) * ds + (1 + u) * p * acc + u * p * np.abs(dd)[:, None] \
         + sub * (p > 0)
     e_dq = scale * (e_ds @ ak + np.abs(dd[:, None] * (p @ k)))
     e_dk = scale * (e_ds.T @ aq + np.abs((p * dd[:, None]).T @ q))
-    e_dv = ((u + rho + ACC) * p + sub * (p > 0)).T @ ado
+    pv = p * zc
+    e_dv = ((u + rho + ACC) * pv + sub * (pv > 0)).T @ ado
     return e_dq + 1e-6, e_dk + 1e-6, e_dv + 1e-6
 
 

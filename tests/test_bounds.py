@@ -58,3 +58,33 @@ def test_bound_catches_a_dropped_rounding():
     dq = sc * coarse @ a[1]
     g = oracle.backward_head(*a, sc, True)
     assert np.any(np.abs(dq - g[0]) > backward_bound(t, *a, o_in, sc, dt)[0])
+
+
+@pytest.mark.parametrize("N,d,dtype,causal,scale,p_drop", [
+    (200, 64, "bf16", True, 1.0, 0.2), (150, 128, "bf16", False, 0.3, 0.5),
+    (180, 64, "f16", True, 0.5, 0.1)])
+def test_dropout_bounds_cover_rounding_emulation(N, d, dtype, causal, scale, p_drop):
+    """The same bounds with the keep mask times 1 / (1 - p) (t["zc"]) cover an
+    emulation of the dropout kernels: P rounded then masked in P V (output
+    scaled by 1 / (1 - p) in fp32, kept in fp32 as o_acc, rounded as o), D
+    from that fp32 output, dS = P (zc dP - D) rounded, dV from the rounded,
+    masked P."""
+    dt = DT[dtype]
+    q, k, v, do = W.draw_qkvdo(1, 1, N, d, dtype, seed=N + 1)
+    a = [f64(x[0, 0]) for x in (q, k, v, do)]
+    t = oracle.backward_head_dropout_terms(*a, scale, p_drop, 77, 1, 0, causal)
+    p, zc = t["p"], t["zc"]
+    o_acc = (rnd(p, dt) * zc) @ a[2]
+    fb_acc = forward_bound(t, *a[:3], scale, dt, out_rounded=False)
+    fb = forward_bound(t, *a[:3], scale, dt)
+    assert np.all(np.abs(o_acc - t["o"]) <= fb_acc)
+    assert np.all(np.abs(rnd(o_acc, dt) - t["o"]) <= fb)
+    d_row = (a[3] * o_acc).sum(axis=1)
+    ds16 = rnd(p * ((a[3] @ a[2].T) * zc - d_row[:, None]), dt)
+    emul = (scale * ds16 @ a[1], scale * ds16.T @ a[0], (rnd(p, dt) * zc).T @ a[3])
+    g = oracle.backward_head_dropout(*a, scale, p_drop, 77, 1, 0, causal)
+    for name, e, ref, bnd in zip(("dq", "dk", "dv"), emul, g,
+                                 backward_bound(t, *a, o_acc, scale, dt)):
+        err = np.abs(e - ref)
+        assert np.all(err <= bnd), name
+        assert bnd.max() <= 8 * err.max() + 1e-5, (name, bnd.max(), err.max())

@@ -292,3 +292,20 @@ def test_sampled_rows_match_the_whole_head(causal):
     dq, _, _ = DR.backward_head_dropout(q, k, v, do, 0.4, p, seed, 2, bh, causal)
     dq_r = DR.dq_rows_dropout(q, k, v, do, 0.4, p, seed, 2, bh, rows, causal)
     np.testing.assert_allclose(dq_r, dq[rows], rtol=0, atol=1e-12)
+
+
+def test_backward_terms_reproduce_the_whole_head():
+    """backward_head_dropout_terms: its P rows sum to 1, its O is
+    forward_head_dropout's, and scale dS K, scale dS^T Q, (P Z / (1 - p))^T dO
+    are backward_head_dropout's gradients."""
+    n, d, p, seed, scale = 50, 8, 0.25, 4242, 0.6
+    q, k, v, do = (RNG.standard_normal((n, d)) for _ in range(4))
+    t = DR.backward_head_dropout_terms(q, k, v, do, scale, p, seed, 3, 2, True)
+    np.testing.assert_allclose(t["p"].sum(axis=1), 1.0, atol=1e-12)
+    o, lse = DR.forward_head_dropout(q, k, v, scale, p, seed, 3, 2, True)
+    np.testing.assert_allclose(t["o"], o, atol=1e-13)
+    np.testing.assert_allclose(t["lse"], lse, atol=1e-13)
+    dq, dk, dv = DR.backward_head_dropout(q, k, v, do, scale, p, seed, 3, 2, True)
+    np.testing.assert_allclose(scale * t["ds"] @ k, dq, atol=1e-12)
+    np.testing.assert_allclose(scale * t["ds"].T @ q, dk, atol=1e-12)
+    np.testing.assert_allclose((t["p"] * t["zc"]).T @ do, dv, atol=1e-12)
