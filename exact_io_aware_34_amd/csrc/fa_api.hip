@@ -94,7 +94,7 @@ bool dropout_args(float p, uint64_t seed, uint32_t offset, uint32_t& k0, uint32_
 int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                  int N, int d, float scale, int causal, const uint8_t* block_mask, int dtype,
                  bool drop, float dropout_p, uint64_t seed, uint32_t offset, float* o_acc,
-                 void* stream);
+                 int* order, void* stream);
 int backward_impl(const void* q, const void* k, const void* v, const void* o, const void* dO,
                   const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, int d,
                   float scale, int causal, const uint8_t* block_mask, int dtype, bool drop,
@@ -156,7 +156,7 @@ int fp8_setup(fa::Fp8Params& p, const void* q, const void* k, const void* v, int
 
 extern "C" {
 
-int fa_abi_version(void) { return 5; }
+int fa_abi_version(void) { return 6; }
 
 const char* fa_status_string(int status) {
   switch (status) {
@@ -173,7 +173,7 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int N, int d, float scale, int causal,
                const uint8_t* block_mask, int dtype, void* stream) {
   return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, dtype, false, 0.f, 0,
-                      0, nullptr, stream);
+                      0, nullptr, nullptr, stream);
 }
 
 int fa_forward_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -181,17 +181,28 @@ int fa_forward_dropout(const void* q, const void* k, const void* v, void* o, flo
                        const uint8_t* block_mask, int dtype, float dropout_p, uint64_t seed,
                        uint32_t offset, float* o_acc, void* stream) {
   return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, dtype, true,
-                      dropout_p, seed, offset, o_acc, stream);
+                      dropout_p, seed, offset, o_acc, nullptr, stream);
 }
 
 }  // extern "C"
 
 namespace {
 
+// The block-sparse forward without the causal flag (16-bit inputs) takes a
+// head's query tiles in the backward's work order, ranked by
+// sparse_order_kernel into `order` (two int32 per 128-row tile) before the
+// forward kernel runs.  Other calls keep the index order.
+hipError_t sparse_forward_order(fa::FwdParams& p, int causal, int dtype, int* order,
+                                hipStream_t st) {
+  if (p.mask == nullptr || causal != 0 || dtype == FA_F32) return hipSuccess;
+  p.qt_order = order;
+  return fa::launch_sparse_order(p.mask, p.mask_tiles, false, order, order + p.mask_tiles, st);
+}
+
 int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                  int N, int d, float scale, int causal, const uint8_t* block_mask, int dtype,
                  bool drop, float dropout_p, uint64_t seed, uint32_t offset, float* o_acc,
-                 void* stream) {
+                 int* order, void* stream) {
   if (!tensor_ptr_ok(q) || !tensor_ptr_ok(k) || !tensor_ptr_ok(v) || !tensor_ptr_ok(o))
     return FA_ERR_INVALID_ARG;
   if (lse == nullptr || !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
@@ -221,6 +232,10 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   p.drop = drop && (p.drop_t8 > 0 || o_acc != nullptr);
   p.o_acc = o_acc;
   if (p.drop && dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (order != nullptr) {
+    const hipError_t e = sparse_forward_order(p, causal, dtype, order, (hipStream_t)stream);
+    if (e != hipSuccess) return FA_ERR_HIP;
+  }
   const hipError_t e = fa::launch_forward(p, dtype, d, causal != 0, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -259,6 +274,12 @@ size_t forward_split_part_bytes(int B, int H, int N, int d, int n) {
   return pad256((size_t)B * H * n * N * d * sizeof(float));
 }
 
+// Both partial-result regions of a split forward with n runs (0 for one run).
+size_t forward_split_parts_bytes(int B, int H, int N, int d, int n) {
+  if (n <= 1) return 0;
+  return forward_split_part_bytes(B, H, N, d, n) + pad256((size_t)B * H * n * N * sizeof(float));
+}
+
 }  // namespace
 
 extern "C" {
@@ -269,8 +290,8 @@ int fa_forward_splits(int B, int H, int N, int d, int n_splits, int dtype) {
 
 size_t fa_forward_split_workspace_size(int B, int H, int N, int d, int n_splits, int dtype) {
   const int n = forward_split_count(B, H, N, d, n_splits, dtype);
-  if (n <= 1) return 0;
-  return forward_split_part_bytes(B, H, N, d, n) + pad256((size_t)B * H * n * N * sizeof(float));
+  if (n < 1) return 0;
+  return forward_split_parts_bytes(B, H, N, d, n) + order_bytes(N);
 }
 
 int fa_forward_split(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -281,9 +302,13 @@ int fa_forward_split(const void* q, const void* k, const void* v, void* o, float
   const int rc = check_common(B, H, N, d, scale, dtype);
   if (rc != FA_OK) return rc;
   const int n = forward_split_count(B, H, N, d, n_splits, dtype);
-  if (n <= 1)
+  if (n <= 1) {
+    // One run: the workspace is optional (only the work order uses it).
+    const bool ws_ok = workspace != nullptr && aligned(workspace, 256) &&
+                       workspace_bytes >= order_bytes(N);
     return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, dtype, false, 0.f,
-                        0, 0, nullptr, stream);
+                        0, 0, nullptr, ws_ok ? (int*)workspace : nullptr, stream);
+  }
   if (!tensor_ptr_ok(q) || !tensor_ptr_ok(k) || !tensor_ptr_ok(v) || !tensor_ptr_ok(o))
     return FA_ERR_INVALID_ARG;
   if (lse == nullptr || !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
@@ -312,7 +337,11 @@ int fa_forward_split(const void* q, const void* k, const void* v, void* o, float
   p.n_splits = n;
   p.o_part = (float*)workspace;
   p.lse_part = (float*)((char*)workspace + forward_split_part_bytes(B, H, N, d, n));
-  hipError_t e = fa::launch_forward(p, dtype, d, causal != 0, (hipStream_t)stream);
+  hipError_t e = sparse_forward_order(
+      p, causal, dtype, (int*)((char*)workspace + forward_split_parts_bytes(B, H, N, d, n)),
+      (hipStream_t)stream);
+  if (e != hipSuccess) return FA_ERR_HIP;
+  e = fa::launch_forward(p, dtype, d, causal != 0, (hipStream_t)stream);
   if (e != hipSuccess) return FA_ERR_HIP;
   fa::DecParams m{};
   m.o = o;

@@ -736,9 +736,7 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
   // dK/dV kernel reads, so it runs first.
   const dim3 grid(((p.N + 127) / 128) * p.BH), block(256);
   if constexpr (SPARSE) {
-    sparse_order_kernel<<<1, 1024, 0, st>>>(p.mask, p.mask_tiles, CAUSAL ? 1 : 0, p.qt_order,
-                                             p.kt_order);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launch_sparse_order(p.mask, p.mask_tiles, CAUSAL, p.qt_order, p.kt_order, st);
     if (e != hipSuccess) return e;
   }
   bwd_dq_u_kernel<T, D, CAUSAL, SPARSE, DROP><<<grid, block, 0, st>>>(p);
@@ -763,6 +761,12 @@ hipError_t launch_bwd(const BwdParams& p, bool causal, bool sparse, hipStream_t 
 }
 
 }  // namespace
+
+hipError_t launch_sparse_order(const uint8_t* mask, int n, bool causal, int* qt_order,
+                               int* kt_order, hipStream_t st) {
+  sparse_order_kernel<<<1, 1024, 0, st>>>(mask, n, causal ? 1 : 0, qt_order, kt_order);
+  return hipGetLastError();
+}
 
 hipError_t launch_backward(BwdParams p, int dtype, int d, bool causal, hipStream_t st) {
   const bool sparse = p.mask != nullptr;

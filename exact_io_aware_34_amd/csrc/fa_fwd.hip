@@ -27,7 +27,9 @@
 //     takes P^T straight from the score accumulators with no shuffle.
 //   * exp is exp2 with scale*log2(e) folded into one FMA.
 //   * Causal grids run longest query tiles first; workgroup ids are remapped
-//     so that all tiles of one head land on one XCD (shared L2).
+//     so that all tiles of one head land on one XCD (shared L2).  Given a
+//     work order, block-sparse grids take a head's query tiles with the most
+//     visible key tiles first.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -79,6 +81,10 @@ __global__ __launch_bounds__(256, fwd16_waves(D, NS)) void fwd16_kernel(FwdParam
     const int lid = xcd_remap(bid, n_qt * p.BH);
     bh = lid / n_qt;
     qt = lid - bh * n_qt;
+    // Block-sparse: the head's query tiles with the most visible key tiles
+    // first, so that the workgroups an XCD runs at once hold rows of similar
+    // length, walk the head's K/V tiles in step and find them in L2.
+    if (SPARSE && p.qt_order != nullptr) qt = p.qt_order[qt];
   }
   const size_t base = (size_t)bh * N * D;
   const T* __restrict__ Q = (const T*)p.q + base;

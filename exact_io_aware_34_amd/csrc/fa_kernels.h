@@ -76,6 +76,9 @@ struct FwdParams {
   void* o;
   float* lse;
   const uint8_t* mask;  // nullptr = dense
+  // Block-sparse without the causal flag, 16-bit inputs: query tiles in
+  // the order to take them (sparse_order_kernel's), nullptr = index order.
+  const int* qt_order;
   int BH, N;
   int n_qtiles, n_ktiles, mask_tiles;
   float scale, scale_log2e;
@@ -168,6 +171,11 @@ struct DropMaskParams {
 };
 
 hipError_t launch_forward(FwdParams p, int dtype, int d, bool causal, hipStream_t st);
+// Block-sparse work order (fa_bwd.hip): the mask's n row tiles and n column
+// tiles ranked by visible tiles, most first (causal: on or below the
+// diagonal), into qt_order[n] and kt_order[n].
+hipError_t launch_sparse_order(const uint8_t* mask, int n, bool causal, int* qt_order,
+                               int* kt_order, hipStream_t st);
 hipError_t launch_backward(BwdParams p, int dtype, int d, bool causal, hipStream_t st);
 hipError_t launch_decode(DecParams p, int dtype, int d, bool causal, hipStream_t st);
 // Merge of per-range partial outputs (o_part, lse_part, n_splits, BH, Nq) into

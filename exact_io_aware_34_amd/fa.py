@@ -180,8 +180,10 @@ def forward(q, k, v, causal=False, scale=None, block_mask=None, out=None, lse=No
     dtype, which the dropout backward needs.  Without dropout the call is
     fa_forward_split: n_splits = 0 (default) lets the library split the key
     range of grids too small to fill the GPU (one run, i.e. fa_forward, for
-    every other grid), 1 never splits, > 1 asks for that many runs;
-    `workspace` is allocated here when None and needed."""
+    every other grid), 1 never splits, > 1 asks for that many runs; a
+    block-sparse call without the causal flag also takes fa_forward_split,
+    whose workspace holds its query-tile work order.  `workspace` is
+    allocated here when None and needed."""
     _check_inputs(q, k, v)
     B, H, N, d = q.shape
     scale = default_scale(d) if scale is None else float(scale)
@@ -195,7 +197,10 @@ def forward(q, k, v, causal=False, scale=None, block_mask=None, out=None, lse=No
     drop = bool(dropout_p) or o_acc is not None
     if drop and n_splits not in (0, 1):
         raise ValueError("split key runs are not offered with dropout")
-    if not drop and fa_forward_splits_used(B, H, N, d, n_splits, q.dtype) > 1:
+    # fa_forward_split also takes the block-sparse (not causal) forward, whose
+    # workspace holds the query-tile work order.
+    ordered = mask is not None and not causal and q.dtype != torch.float32
+    if not drop and (ordered or fa_forward_splits_used(B, H, N, d, n_splits, q.dtype) > 1):
         ws_bytes = forward_split_workspace_size(B, H, N, d, n_splits, q.dtype)
         if workspace is None and ws_bytes > 0:
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)

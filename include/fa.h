@@ -93,12 +93,19 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
  * one round, with at least ten 64-key tiles per run (for FA_F32 inputs, whose
  * tiles take the matrix cores far longer: enough runs for one workgroup per
  * CU, at least two tiles each).  An explicit n_splits is
- * capped at ceil(N / 64) and at 64.  With one run this is fa_forward and no
- * workspace is used.  `workspace` (at least
- * fa_forward_split_workspace_size() bytes, 256-byte aligned, caller-owned,
- * contents ignored on entry) holds the partial results, in this order, each
- * region padded to 256 bytes: o_part (B*H, n, N, d) fp32, lse_part (B*H, n, N)
- * fp32.  Supported: every dtype and head dimension fa_forward supports;
+ * capped at ceil(N / 64) and at 64.  With one run this is fa_forward.
+ * `workspace` (at least fa_forward_split_workspace_size() bytes, 256-byte
+ * aligned, caller-owned, contents ignored on entry) holds, in this order,
+ * each region padded to 256 bytes: o_part (B*H, n, N, d) fp32 and lse_part
+ * (B*H, n, N) fp32 (both only when n > 1), then the block-sparse work order,
+ * two int32 per 128-row tile.  With a block_mask, no causal flag and 16-bit
+ * inputs, the forward takes each head's query tiles in the backward's work
+ * order (most visible key tiles first, ties by index): workgroups that run at once then hold rows of similar
+ * length, walk the head's K/V tiles in step and find them in L2; every
+ * tile's arithmetic is unchanged, so o and lse are bit-identical to
+ * fa_forward's.  With one run the workspace is optional: when it is null,
+ * misaligned or smaller than the order, the tiles run in index order.
+ * Supported: every dtype and head dimension fa_forward supports;
  * B*H*n*N < 2^31, else FA_ERR_UNSUPPORTED; n_splits < 0 -> FA_ERR_INVALID_ARG.
  */
 int fa_forward_split(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -110,8 +117,8 @@ int fa_forward_split(const void* q, const void* k, const void* v, void* o, float
  * (0 on bad input). */
 int fa_forward_splits(int B, int H, int N, int d, int n_splits, int dtype);
 
-/* Bytes of workspace fa_forward_split needs (0 when it uses one run or on bad
- * input). */
+/* Bytes of workspace fa_forward_split needs: the partial results when it uses
+ * more than one run, plus the work order (0 on bad input). */
 size_t fa_forward_split_workspace_size(int B, int H, int N, int d, int n_splits, int dtype);
 
 /* Bytes of device workspace fa_backward needs for this shape (0 on bad input):
@@ -322,12 +329,13 @@ size_t fa_forward_fp8_workspace_size(int B, int H, int N, int d);
 /* Static, human-readable text for a status code. */
 const char* fa_status_string(int status);
 
-/* Library ABI version (this header: 5; 2 added fa_forward_split*, 3 the fp32
+/* Library ABI version (this header: 6; 2 added fa_forward_split*, 3 the fp32
  * output o_acc of the dropout calls, 4 power-of-two FP8 block scales, the
  * scale argument of fa_fp8_prepare and the dtype argument of
  * fa_forward_splits and fa_forward_split_workspace_size, 5 fa_forward_fp8
  * no longer writing the Q regions of its workspace, and `signs` 16-byte
- * aligned). */
+ * aligned, 6 the work order at the end of the fa_forward_split workspace,
+ * also for one run). */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

@@ -68,7 +68,7 @@ def test_header_declares_the_boundary():
 def test_every_declared_symbol_is_exported(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.fa_abi_version() == 5
+    assert lib.fa_abi_version() == 6
 
 
 def test_status_strings(lib):
@@ -306,12 +306,16 @@ def test_forward_split_choice(lib):
 def test_forward_split_workspace_size(lib):
     def W(B, H, N, d, n, dtype=2):
         return lib.fa_forward_split_workspace_size(B, H, N, d, n, dtype)
-    assert W(4, 12, 8192, 64, 0) == 0          # one run
-    assert W(1, 1, 300, 64, 1) == 0
-    # 6 runs of 4096 rows x 64 fp32, then 6 x 4096 fp32
-    assert W(1, 1, 4096, 64, 0) == 6 * 4096 * 64 * 4 + 6 * 4096 * 4
-    assert W(1, 2, 300, 128, 3) == 2 * 3 * 300 * 128 * 4 + (-(-2 * 3 * 300 * 4 // 256)) * 256
-    assert W(1, 1, 256, 64, 0, 0) == 2 * 256 * 64 * 4 + 2 * 256 * 4      # fp32: 2 runs
+    def order(N):  # block-sparse work order: two int32 per 128-row tile, padded to 256 bytes
+        return -(-(2 * -(-N // 128) * 4) // 256) * 256
+    assert W(4, 12, 8192, 64, 0) == order(8192) == 512     # one run: the order only
+    assert W(1, 1, 300, 64, 1) == order(300) == 256
+    # 6 runs of 4096 rows x 64 fp32, then 6 x 4096 fp32, then the order
+    assert W(1, 1, 4096, 64, 0) == 6 * 4096 * 64 * 4 + 6 * 4096 * 4 + 256
+    assert W(1, 2, 300, 128, 3) == (2 * 3 * 300 * 128 * 4 + (-(-2 * 3 * 300 * 4 // 256)) * 256
+                                    + 256)
+    assert W(1, 1, 256, 64, 0, 0) == 2 * 256 * 64 * 4 + 2 * 256 * 4 + 256  # fp32: 2 runs
+    assert W(1, 1, 2048 * 128, 64, 1) == 2 * 2048 * 4
     assert W(1, 1, 256, 64, 0, 9) == 0
 
 

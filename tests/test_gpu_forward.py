@@ -161,3 +161,28 @@ def test_forward_large_grid_block_sparse(fa):
     for (b, h), (ro, rl) in zip(heads, oracle_forward_heads(q, k, v, scale, False, mask, heads)):
         assert_close(f"o[{b},{h}]", f64(o[b, h]), ro, TOL[torch.float16])
         assert_close(f"lse[{b},{h}]", f64(lse[b, h]), rl, LSE_TOL)
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype", [(1, 3, 2000, 64, "bf16"), (2, 2, 1500, 128, "f16")])
+def test_block_sparse_work_order_is_bit_exact(fa, B, H, N, d, dtype):
+    """fa.forward sends a block-sparse call without the causal flag through
+    fa_forward_split with a workspace, where each head's query tiles run in
+    the work order (most visible key tiles first).  A tile's arithmetic does
+    not depend on when it runs, so o and lse equal those of fa_forward (index
+    order) bit for bit; the mask's rows differ in length, so the order is not
+    the index order."""
+    q, k, v, _ = W.draw_qkvdo(B, H, N, d, dtype, seed=N)
+    mask = random_block_mask(N, 0.4, seed=N + 1)
+    counts = mask.sum(dim=1)
+    assert not bool((counts[:-1] >= counts[1:]).all())          # not already sorted
+    qd, kd, vd, md = (t.cuda() for t in (q, k, v, mask))
+    scale = W.scale_for(d)
+    o, lse = fa.forward(qd, kd, vd, causal=False, scale=scale, block_mask=md, n_splits=1)
+    o_idx, lse_idx = torch.empty_like(qd), torch.empty_like(lse)
+    rc = fa._lib.fa_forward(fa._ptr(qd), fa._ptr(kd), fa._ptr(vd), fa._ptr(o_idx),
+                            fa._ptr(lse_idx), B, H, N, d, scale, 0, fa._ptr(md),
+                            fa.DTYPE_CODES[qd.dtype], fa._stream(None))
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_idx)
+    assert torch.equal(lse, lse_idx)
