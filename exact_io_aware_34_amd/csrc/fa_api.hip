@@ -103,7 +103,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
 
 // FP8 workspace regions, in order, each padded to 256 bytes.
 struct Fp8Layout {
-  size_t q8, k8, v8t, sq, sk, sv, total;
+  size_t q8, k8, v8t, sq, sk, sv, order, total;
 };
 
 Fp8Layout fp8_layout(int B, int H, int N, int d) {
@@ -116,7 +116,8 @@ Fp8Layout fp8_layout(int B, int H, int N, int d) {
   l.sq = 3 * op;
   l.sk = 3 * op + sc;
   l.sv = 3 * op + 2 * sc;
-  l.total = 3 * op + 3 * sc;
+  l.order = 3 * op + 3 * sc;
+  l.total = l.order + order_bytes(N);
   return l;
 }
 
@@ -480,6 +481,14 @@ int fa_forward_fp8(const void* q, const void* k, const void* v, void* o, float* 
   p.lse = lse;
   p.mask = block_mask;
   p.prep_z0 = 1;   // K and V; each query tile's Q is prepared by the attention kernel
+  if (block_mask != nullptr && causal == 0) {
+    // The block-sparse work order, as in the 16-bit forward.
+    int* order = (int*)((char*)workspace + fp8_layout(B, H, N, d).order);
+    const hipError_t e = fa::launch_sparse_order(block_mask, p.mask_tiles, false, order,
+                                                 order + p.mask_tiles, (hipStream_t)stream);
+    if (e != hipSuccess) return FA_ERR_HIP;
+    p.qt_order = order;
+  }
   const hipError_t e = fa::launch_fp8(p, dtype, d, causal != 0, true, true, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

@@ -269,6 +269,9 @@ __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
     const int lid = xcd_remap(blockIdx.x, n_qt * p.BH);
     bh = lid / n_qt;
     qt = lid - bh * n_qt;
+    // Block-sparse: the 16-bit forward's work order (most visible key tiles
+    // first), for the same L2 reuse.
+    if (SPARSE && p.qt_order != nullptr) qt = p.qt_order[qt];
   }
   const uint8_t* __restrict__ K8 = p.k8 + (size_t)bh * p.Npad * D;
   const uint8_t* __restrict__ V8 = p.v8t + (size_t)bh * nt * TB;

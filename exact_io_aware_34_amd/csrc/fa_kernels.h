@@ -148,6 +148,9 @@ struct Fp8Params {
   void* o;        // (B*H, N, d), dtype of q
   float* lse;     // (B*H, N)
   const int8_t* signs;  // d random signs of the rotation, nullptr = no rotation
+  // Block-sparse without the causal flag: query tiles in the order to take
+  // them (workspace, sparse_order_kernel's), nullptr = index order.
+  const int* qt_order;
   // Prepared operands (workspace): Q8, K8 (B*H, Npad, d) E4M3 row-major;
   // V8^T (B*H, n_t64, d, 64) E4M3, keys of a block permuted; one fp32 scale
   // per (b*h, 64-row block) of each.

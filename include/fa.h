@@ -307,7 +307,10 @@ int fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, floa
  *   V8T (B*H, nt, d, 64) E4M3 codes of each 64-key block transposed, position
  *       32 g + e holding key 32 (e / 16) + 8 ((e % 16) / 4) + 4 g + e % 4 of
  *       the block (keys >= N are zero)
- *   s_q, s_k, s_v (B*H, nt) fp32 block scales.
+ *   s_q, s_k, s_v (B*H, nt) fp32 block scales
+ *   the block-sparse work order, two int32 per 128-row tile (written and
+ *   used by fa_forward_fp8 with a block_mask and no causal flag: each head's
+ *   query tiles run in the order fa_forward_split gives them).
  * Supported: d in {64, 128}; FA_F32 -> FA_ERR_UNSUPPORTED.
  */
 int fa_forward_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -335,7 +338,7 @@ const char* fa_status_string(int status);
  * fa_forward_splits and fa_forward_split_workspace_size, 5 fa_forward_fp8
  * no longer writing the Q regions of its workspace, and `signs` 16-byte
  * aligned, 6 the work order at the end of the fa_forward_split workspace,
- * also for one run). */
+ * also for one run, and of the fa_forward_fp8 workspace). */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

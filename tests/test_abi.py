@@ -206,9 +206,10 @@ def test_decode_validation(lib):
 
 def test_fp8_workspace_size(lib):
     W = lib.fa_forward_fp8_workspace_size
-    # 3 operand regions of B*H*Npad*d bytes + 3 scale regions of B*H*nt fp32, each padded to 256
-    assert W(4, 12, 8192, 64) == 3 * 48 * 8192 * 64 + 3 * 48 * 128 * 4
-    assert W(1, 1, 65, 128) == 3 * 128 * 128 + 3 * 256
+    # 3 operand regions of B*H*Npad*d bytes + 3 scale regions of B*H*nt fp32, then the
+    # block-sparse work order (two int32 per 128-row tile), each padded to 256
+    assert W(4, 12, 8192, 64) == 3 * 48 * 8192 * 64 + 3 * 48 * 128 * 4 + 512
+    assert W(1, 1, 65, 128) == 3 * 128 * 128 + 3 * 256 + 256
     assert W(0, 1, 64, 64) == 0
 
 

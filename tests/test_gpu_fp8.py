@@ -238,6 +238,9 @@ FWD_CASES = [
     (1, 2, 384, 128, "bf16", True, None, True),
     (1, 1, 200, 128, "f16", False, None, False),
     (2, 3, 128, 64, "bf16", True, None, False),
+    # block-sparse without the causal flag: query tiles in the work order
+    (1, 2, 900, 128, "bf16", False, "holed", True),
+    (2, 1, 1100, 64, "f16", False, "holed", False),
 ]
 
 
