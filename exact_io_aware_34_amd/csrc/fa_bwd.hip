@@ -93,9 +93,8 @@ __global__ __launch_bounds__(256, dkdv_waves(D)) void bwd_dkdv_u_kernel(BwdParam
     bh = lid / n_kt;
     j = p.kt_order[lid - bh * n_kt];
   } else if (CAUSAL) {
-    // Key tiles with the most query tiles (small j) first across all heads.
-    bh = blockIdx.x % p.BH;
-    j = blockIdx.x / p.BH;
+    // Key tiles with the most query tiles (small j) first, few heads per XCD.
+    causal_tile(blockIdx.x, p.BH, n_kt, bh, j);
   } else {
     const int lid = xcd_remap(blockIdx.x, n_kt * p.BH);
     bh = lid / n_kt;
@@ -420,8 +419,9 @@ __global__ __launch_bounds__(256, bwd_u_waves(D)) void bwd_dq_u_kernel(BwdParams
     bh = lid / n_qt;
     qt = p.qt_order[lid - bh * n_qt];
   } else if (CAUSAL) {
-    bh = blockIdx.x % p.BH;
-    qt = n_qt - 1 - blockIdx.x / p.BH;
+    int rank;
+    causal_tile(blockIdx.x, p.BH, n_qt, bh, rank);
+    qt = n_qt - 1 - rank;
   } else {
     const int lid = xcd_remap(blockIdx.x, n_qt * p.BH);
     bh = lid / n_qt;

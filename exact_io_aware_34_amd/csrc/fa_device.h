@@ -385,4 +385,32 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
   return (x < rem) ? x * (per + 1) + r : rem * (per + 1) + (x - rem) * per + r;
 }
 
+// Causal work order: workgroup id -> (head, rank), rank k being each head's
+// k-th longest tile.  Ranks run longest first (a list schedule in order of
+// decreasing work) and each XCD works on as few heads as an even split of
+// the work allows.  The hardware deals ids to the 8 XCDs round robin, so
+// XCD x runs ids 8r + x in order of r.  With P = 8 / gcd(BH, 8) ranks per
+// period, the BH*P tiles of a period go to the XCDs head-major, Q = BH*P/8
+// consecutive (head, rank) pairs each: whole heads when BH is a multiple of
+// 8, one head and alternate ranks of a second for 12 heads, instead of
+// every head on every XCD.  The ranks past the last whole period (the
+// shortest tiles) take the heads round robin.
+__device__ __forceinline__ void causal_tile(int bid, int BH, int n_rank, int& bh, int& rank) {
+  const int low = BH & -BH;
+  const int P = 8 / (low < 8 ? low : 8);  // 1, 2, 4 or 8
+  const int Q = BH * P / 8;
+  const int periods = n_rank / P;
+  const int n_full = periods * P * BH;
+  if (bid < n_full) {
+    const int x = bid & 7, r = bid >> 3;
+    const int period = r / Q, t = x * Q + (r - period * Q);
+    bh = t / P;
+    rank = period * P + (t - bh * P);
+  } else {
+    const int b = bid - n_full;
+    bh = b % BH;
+    rank = periods * P + b / BH;
+  }
+}
+
 }  // namespace fa

@@ -263,8 +263,9 @@ __global__ __launch_bounds__(256, fwd8_waves(D)) void fwd8_kernel(Fp8Params p) {
   const int n_qt = (N + BR - 1) / BR;
   int bh, qt;
   if (CAUSAL) {
-    bh = blockIdx.x % p.BH;
-    qt = n_qt - 1 - blockIdx.x / p.BH;
+    int rank;
+    causal_tile(blockIdx.x, p.BH, n_qt, bh, rank);
+    qt = n_qt - 1 - rank;
   } else {
     const int lid = xcd_remap(blockIdx.x, n_qt * p.BH);
     bh = lid / n_qt;

@@ -72,11 +72,10 @@ __global__ __launch_bounds__(256, fwd16_waves(D, NS)) void fwd16_kernel(FwdParam
   }
   int bh, qt;
   if (CAUSAL) {
-    // Longest query tiles first across all heads (a list schedule in order
-    // of decreasing work); with B*H a multiple of 8 the round-robin XCD
-    // assignment still gives every XCD whole heads.
-    bh = bid % p.BH;
-    qt = n_qt - 1 - bid / p.BH;
+    // Longest query tiles first, few heads per XCD (causal_tile).
+    int rank;
+    causal_tile(bid, p.BH, n_qt, bh, rank);
+    qt = n_qt - 1 - rank;
   } else {
     const int lid = xcd_remap(bid, n_qt * p.BH);
     bh = lid / n_qt;
