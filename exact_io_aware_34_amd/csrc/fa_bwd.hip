@@ -704,18 +704,36 @@ __global__ __launch_bounds__(1024) void sparse_order_kernel(const uint8_t* __res
   for (int i = tid; i < n; i += 1024) col_n[i] = 0;
   __syncthreads();
   // Tile (r, c) counts for row r and column c when it is set (and, causal,
-  // c <= r).  A wave reads one mask row at a time, 64 columns per step: the
-  // row count is the popcount of the step ballots, the column counts LDS
-  // atomic adds.
-  for (int r = wave; r < n; r += 16) {
-    int rc = 0;
+  // c <= r).  A wave takes RB mask rows at a time (rows wave, wave + 16, ...),
+  // 64 columns per step, loading the step's RB bytes per lane before using
+  // any (one memory latency per step, not per row): the row count is the
+  // popcount of the step ballots, the column counts LDS atomic adds.
+  constexpr int RB = 8;
+  for (int r0 = wave; r0 < n; r0 += 16 * RB) {
+    int rc[RB] = {};
     for (int c0 = 0; c0 < n; c0 += 64) {
       const int c = c0 + lane;
-      const bool vis = c < n && mask[(size_t)r * n + c] != 0 && (!causal || c <= r);
-      rc += __popcll(__builtin_amdgcn_ballot_w64(vis));
-      if (vis) atomicAdd(&col_n[c], 1);
+      // Clamped addresses, so that the loads are unconditional and issue
+      // together; the out-of-range bytes are dropped after.
+      uint8_t m[RB];
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const int r = r0 + 16 * i;
+        m[i] = mask[(size_t)min(r, n - 1) * n + min(c, n - 1)];
+      }
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+        if (r0 + 16 * i >= n || c >= n) m[i] = 0;
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const bool vis = m[i] != 0 && (!causal || c <= r0 + 16 * i);
+        rc[i] += __popcll(__builtin_amdgcn_ballot_w64(vis));
+        if (vis) atomicAdd(&col_n[c], 1);
+      }
     }
-    if (lane == 0) row_n[r] = rc;
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+      if (lane == 0 && r0 + 16 * i < n) row_n[r0 + 16 * i] = rc[i];
   }
   __syncthreads();
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
