@@ -249,11 +249,13 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
 // causal and not) this choice was the fastest count on every one; runs
 // shorter than ~10 tiles spend most of their time filling and draining the
 // copy pipeline.  An fp32 tile costs the matrix cores ~16 times as long, so
-// for fp32 inputs two tiles per run already cover the fill and one
-// workgroup per CU (256) is enough: one head at d = 64 took 91.6 us in one
-// run and 26 us in eight at N = 1024, 29.4 us in one and 22.5 us in two at
-// N = 256, and 77-80 us in 6 to 24 runs at N = 4096.  An explicit count is
-// capped at the number of 64-key tiles.
+// for fp32 inputs one 64-key tile per run already covers the fill and one
+// workgroup per CU (256) is enough: one head at d = 64 took 89.8 us in one
+// run, 21.3 in eight and 19.6 in sixteen at N = 1024, 30.4 us in two, 20.3
+// in four and 19.4 in eight at N = 512, 27.3 us in one and 20 in two or
+// four at N = 256, and 57.5 us in eight (its count here) against 59.8-85.7
+// in 16-64 at N = 4096.  An explicit count is capped at the number of
+// 64-key tiles.
 int forward_split_count(int B, int H, int N, int d, int n_splits, int dtype) {
   if (B < 1 || H < 1 || N < 1 || n_splits < 0 || (d != 64 && d != 128)) return 0;
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return 0;
@@ -261,7 +263,7 @@ int forward_split_count(int B, int H, int N, int d, int n_splits, int dtype) {
   const long long wgs = (long long)B * H * ((N + 127) / 128);
   const long long round = d == 64 ? 768 : 512;
   const long long target = dtype == FA_F32 ? 256 : round;
-  const long long min_run = dtype == FA_F32 ? 2 : 10;
+  const long long min_run = dtype == FA_F32 ? 1 : 10;
   long long n = n_splits;
   if (n == 0) {
     n = 1;

@@ -92,7 +92,7 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
  * the GPU (768 workgroups at d = 64, 512 at d = 128), then enough runs for
  * one round, with at least ten 64-key tiles per run (for FA_F32 inputs, whose
  * tiles take the matrix cores far longer: enough runs for one workgroup per
- * CU, at least two tiles each).  An explicit n_splits is
+ * CU, at least one tile each).  An explicit n_splits is
  * capped at ceil(N / 64) and at 64.  With one run this is fa_forward.
  * `workspace` (at least fa_forward_split_workspace_size() bytes, 256-byte
  * aligned, caller-owned, contents ignored on entry) holds, in this order,

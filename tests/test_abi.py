@@ -286,13 +286,13 @@ def test_forward_split_choice(lib):
     assert S(1, 1, 256, 64, 0) == 1            # 4 key tiles
     assert S(1, 1, 1000, 64, 0) == 1           # 16 key tiles: one run of >= 10
     assert S(1, 1, 1000, 64, 0, 1) == 1        # fp16: the same rule
-    # fp32 inputs: 256 workgroups wanted, runs of >= 2 key tiles
-    assert S(1, 1, 256, 64, 0, 0) == 2         # 4 key tiles
-    assert S(1, 1, 1000, 64, 0, 0) == 8        # 16 key tiles, 8 query tiles -> 32 wanted
+    # fp32 inputs: 256 workgroups wanted, runs of >= 1 key tile
+    assert S(1, 1, 256, 64, 0, 0) == 4         # 4 key tiles, one per run
+    assert S(1, 1, 1000, 64, 0, 0) == 16       # 16 key tiles, 8 query tiles -> 32 wanted
     assert S(1, 1, 4096, 64, 0, 0) == 8        # 32 query tiles -> 8 wanted
     assert S(1, 4, 8192, 64, 0, 0) == 1        # 256 query tiles
     assert S(4, 12, 8192, 64, 0, 0) == 1       # full grid
-    assert S(1, 1, 100, 64, 0, 0) == 1         # 2 key tiles
+    assert S(1, 1, 100, 64, 0, 0) == 2         # 2 key tiles, one per run
     # Explicit counts are capped at the key tiles and at 64.
     assert S(1, 1, 300, 64, 9) == 5
     assert S(1, 1, 1 << 16, 64, 100) == 64
@@ -315,7 +315,7 @@ def test_forward_split_workspace_size(lib):
     assert W(1, 1, 4096, 64, 0) == 6 * 4096 * 64 * 4 + 6 * 4096 * 4 + 256
     assert W(1, 2, 300, 128, 3) == (2 * 3 * 300 * 128 * 4 + (-(-2 * 3 * 300 * 4 // 256)) * 256
                                     + 256)
-    assert W(1, 1, 256, 64, 0, 0) == 2 * 256 * 64 * 4 + 2 * 256 * 4 + 256  # fp32: 2 runs
+    assert W(1, 1, 256, 64, 0, 0) == 4 * 256 * 64 * 4 + 4 * 256 * 4 + 256  # fp32: 4 runs
     assert W(1, 1, 2048 * 128, 64, 1) == 2 * 2048 * 4
     assert W(1, 1, 256, 64, 0, 9) == 0
 
